@@ -1,0 +1,260 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+Headline: one engine step of the Qwen3-0.6B-shaped decode workload (batch 64, 16 q heads /
+8 kv heads, head_dim 128, bf16, context U[256, 4096], block 256, 2048-block pool): store
+the 64 new tokens' K/V with store_kvcache, then paged_attn_decode (split-K partials + the
+combine). Consecutive steps rotate over several layer pools (each a full copy of the
+2048-block K/V pool, as every layer of the engine owns its own cache), so the KV read
+streams from HBM rather than from the 256 MB last-level cache.
+
+The same JSON line also carries the prefill half of the metric (the varlen prefill and
+the prefix-cached prefill workloads, in TFLOP/s against the bf16 MFMA peak), the large
+decode workload (512 sequences, shared prefixes) and the host metadata time.
+
+``value`` is the decode step's algorithmic bytes per second (KV rows of every visible key
+once per sequence and kv head, plus q, out, tables, and the store's reads and writes).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode paged-attn KV GB/s (% HBM peak); prefill attn TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+# ---------------------------------------------------------------- algorithmic work
+def decode_bytes(w, unique=False):
+    e = w.elem_bytes
+    row = w.num_kv_heads * w.head_dim * e           # one token's K (or V) row, all kv heads
+    if unique:
+        prefix_used = int(w.shared_blocks.max()) if len(w.shared_blocks) else 0
+        toks = int((w.seq_lens - w.shared_blocks * w.block_size).sum()) + prefix_used * w.block_size
+    else:
+        toks = int(w.seq_lens.sum())
+    kv = 2 * toks * row
+    qo = 2 * w.num_seqs * w.num_heads * w.head_dim * e
+    meta = w.num_seqs * (w.max_table_len() * 4 + 4)
+    return kv + qo + meta, kv
+
+
+def store_bytes(w):
+    n_new = int(w.q_lens.sum())
+    row = w.num_kv_heads * w.head_dim * w.elem_bytes
+    return 2 * 2 * n_new * row + 4 * n_new
+
+
+def prefill_flops(w):
+    Lq = w.q_lens.astype(np.int64)
+    Lk = w.seq_lens.astype(np.int64)
+    pairs = int((Lq * (Lk - Lq) + Lq * (Lq + 1) // 2).sum())
+    return 4 * w.num_heads * w.head_dim * pairs, pairs
+
+
+# ---------------------------------------------------------------- GPU legs
+def _median_event_ms(torch, fn, iters, warmup, stream):
+    for _ in range(warmup):
+        fn()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    torch.cuda.synchronize()
+    for i in range(iters):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
+
+
+def bench_decode_headline(torch, args):
+    from paged_kv_cache_225_amd.harness import DeviceStep
+    from workloads import CONFIG_NAMES, make_config
+    w = make_config(2)
+    base = DeviceStep(w)
+    layers = [(base.k_cache, base.v_cache)]
+    for _ in range(args.layers - 1):
+        layers.append((base.k_cache.clone(), base.v_cache.clone()))
+    stream = torch.cuda.current_stream()
+    from paged_kv_cache_225_amd import _binding as B
+
+    def step(i):
+        kc, vc = layers[i % len(layers)]
+        B.store_kvcache(base.new_k, base.new_v, kc, vc, base.slot_mapping, stream=stream)
+        B.paged_attn_decode(base.out, base.q, kc, vc, base.block_tables, base.context_lens,
+                            w.scale, workspace=base.workspace, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    # timed region: exactly K steps between two synchronisations; the decode call of each
+    # step is bracketed by events on the launch stream for the per-launch kernel time
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        kc, vc = layers[i % len(layers)]
+        B.store_kvcache(base.new_k, base.new_v, kc, vc, base.slot_mapping, stream=stream)
+        ev[i][0].record(stream)
+        B.paged_attn_decode(base.out, base.q, kc, vc, base.block_tables, base.context_lens,
+                            w.scale, workspace=base.workspace, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    step_bytes_dec, kv = decode_bytes(w)
+    step_bytes = step_bytes_dec + store_bytes(w)
+    ms_per_step = elapsed * 1e3 / args.steps
+    dec_avg = float(dec_ms.mean())
+    achieved = step_bytes_dec / (dec_avg * 1e-3) / 1e9
+    return {
+        "w": w,
+        "name": CONFIG_NAMES[2],
+        "ms_per_step": ms_per_step,
+        "value": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "tokens_per_s": w.num_seqs / (ms_per_step * 1e-3),
+        "step_bytes": step_bytes,
+        "kv_bytes": kv,
+        "decode_call_us_avg": dec_avg * 1e3,
+        "decode_call_us_p10_p90": [float(np.percentile(dec_ms, 10)) * 1e3,
+                                   float(np.percentile(dec_ms, 90)) * 1e3],
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+    }
+
+
+def bench_prefill(torch, cfg, iters, warmup):
+    from paged_kv_cache_225_amd.harness import DeviceStep
+    from workloads import CONFIG_NAMES, make_config
+    w = make_config(cfg)
+    ds = DeviceStep(w)
+    stream = torch.cuda.current_stream()
+    ds.store(stream)
+    med, p10, p90 = _median_event_ms(torch, lambda: ds.attend(stream), iters, warmup, stream)
+    st_med, _, _ = _median_event_ms(torch, lambda: ds.store(stream), iters, warmup, stream)
+    flops, pairs = prefill_flops(w)
+    tf = flops / (med * 1e-3) / 1e12
+    return {"workload": CONFIG_NAMES[cfg], "attn_us_median": med * 1e3, "attn_us_p10_p90": [p10 * 1e3, p90 * 1e3],
+            "flops": flops, "tflops": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
+            "tokens_per_s": float(w.q_lens.sum()) / (med * 1e-3),
+            "store_us_median": st_med * 1e3, "store_gbs": store_bytes(w) / (st_med * 1e-3) / 1e9}
+
+
+def bench_large_decode(torch, iters, warmup):
+    from paged_kv_cache_225_amd.harness import DeviceStep
+    from workloads import CONFIG_NAMES, make_config
+    w = make_config(5)
+    ds = DeviceStep(w)
+    stream = torch.cuda.current_stream()
+    ds.store(stream)
+    med, p10, p90 = _median_event_ms(torch, lambda: ds.attend(stream), iters, warmup, stream)
+    uniq, kv_u = decode_bytes(w, unique=True)
+    logi, kv_l = decode_bytes(w, unique=False)
+    return {"workload": CONFIG_NAMES[5], "decode_us_median": med * 1e3,
+            "decode_us_p10_p90": [p10 * 1e3, p90 * 1e3],
+            "unique_gbs": uniq / (med * 1e-3) / 1e9, "logical_gbs": logi / (med * 1e-3) / 1e9,
+            "frac_hbm_unique": uniq / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tokens_per_s": w.num_seqs / (med * 1e-3), "shared_hist": w.meta.get("shared_hist")}
+
+
+def host_metadata_us(w, reps=20):
+    from paged_kv_cache_225_amd import _binding as B
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        B.pkv_decode_metadata(w.seq_lens, w.block_tables, w.block_size)
+    return (time.perf_counter() - t0) / reps * 1e6
+
+
+# ---------------------------------------------------------------- CPU baseline (oracle)
+def cpu_baseline(w, budget_s):
+    from threadpoolctl import threadpool_info
+    from tests.oracle_pipeline import setup_pools, run_step
+    kc, vc = setup_pools(w)
+    step_bytes_dec, _ = decode_bytes(w)
+    step_bytes = step_bytes_dec + store_bytes(w)
+    reps, t_total = 0, 0.0
+    while t_total < budget_s or reps == 0:
+        t0 = time.perf_counter()
+        run_step(w, kc, vc)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": step_bytes * reps / t_total / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{reps} full decode step(s) of the batch-64 workload (store of 64 tokens "
+                      f"+ fp64 attention over all 64 sequences), {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--layers", type=int, default=4, help="layer pools rotated over")
+    ap.add_argument("--iters", type=int, default=50, help="timed runs of the secondary workloads")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    print("bench: decode headline", file=sys.stderr, flush=True)
+    head = bench_decode_headline(torch, args)
+    w = head.pop("w")
+    line = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": head["name"], "global_batch": 64, "heads_q": 16, "heads_kv": 8,
+                   "head_dim": 128, "block_size": 256, "pool_blocks": 2048,
+                   "context": "uniform[256,4096]", "layer_pools_rotated": args.layers,
+                   "step": "store_kvcache(64 tokens) + paged_attn_decode"},
+        "roofline": head["roofline"],
+        "tokens_per_s": head["tokens_per_s"],
+        "decode_call_us_avg": head["decode_call_us_avg"],
+        "decode_call_us_p10_p90": head["decode_call_us_p10_p90"],
+        "step_bytes": head["step_bytes"],
+        "kv_bytes": head["kv_bytes"],
+        "host_metadata_us": host_metadata_us(w),
+    }
+    if not args.no_secondary:
+        print("bench: prefill workloads", file=sys.stderr, flush=True)
+        line["prefill"] = [bench_prefill(torch, 3, args.iters, 5), bench_prefill(torch, 4, args.iters, 5)]
+        print("bench: large decode workload", file=sys.stderr, flush=True)
+        line["large_decode"] = bench_large_decode(torch, args.iters, 5)
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+/*
+ * paged_kv.h - C ABI of the paged-attention hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the nano-vLLM engine described on three pages:
+ *   [P1] "vLLM 学习笔记 02：nano-vllm 源码逐段精读" (listings ModelRunner.prepare_prefill,
+ *        prepare_block_tables, prepare_decode, store_kvcache, Attention.forward, Context)
+ *   [P2] "Nano-vLLM代码手撕笔记" (sections 请求执行 – 输入序列预处理与context构建,
+ *        请求执行 – run model, cuda graph捕捉与context设置)
+ *   [P3] "Nano-vLLM 代码解析" (section 4.2.1 输入准备)
+ *
+ * Conventions for every call:
+ *   - Sizes are element counts unless named *_bytes. Hq = num_heads, Hkv = num_kv_heads,
+ *     D = head_dim, bs = block_size, G = Hq / Hkv.
+ *   - The paged cache of one layer is a pair of arrays k_cache, v_cache of shape
+ *     [num_blocks, bs, Hkv, D], contiguous: physical slot s = block * bs + offset holds
+ *     Hkv * D contiguous elements ([P1] store_kvcache asserts; [P1] allocate_kv_cache).
+ *   - Query head h reads kv head h / G (contiguous head groups, as tensor parallelism
+ *     splits heads in [P1] QKVParallelLinear).
+ *   - "device" pointers are HIP device memory owned by the caller; the library never
+ *     allocates, frees or keeps them. "host" pointers are ordinary host memory.
+ *   - Device calls enqueue on `stream` (0 = the null stream) and never synchronise the host.
+ *   - Every call returns PKV_OK or a negative status; nothing throws across the ABI.
+ *     Host-checkable argument errors are reported before anything is enqueued.
+ *     Data-dependent preconditions (slot and block-id ranges, lengths) are documented
+ *     per call; the kernels bounds-check them so that a violation never reads or writes
+ *     outside the caller's arrays (see each call for what it does instead).
+ */
+#ifndef PAGED_KV_H_
+#define PAGED_KV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype_t;
+
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = -1,     /* null pointer, negative size, inconsistent arguments */
+  PKV_ERR_UNSUPPORTED = -2, /* a valid shape or dtype this build does not implement */
+  PKV_ERR_WORKSPACE = -3,   /* decode workspace smaller than the query function asks */
+  PKV_ERR_HIP = -4          /* a HIP launch error */
+};
+
+/* Human-readable name of a status code (static storage). */
+const char* pkv_status_string(int status);
+
+/* ------------------------------------------------------------------------------------
+ * Host metadata (the harness step before the kernels).
+ *
+ * pkv_prefill_metadata - [P1] ModelRunner.prepare_prefill and prepare_block_tables;
+ * pinned by the worked example of [P2] 请求执行 – 输入序列预处理与context构建.
+ * Sequence b computes positions start = num_cached[b] .. end-1, end = start + num_scheduled[b]
+ * (start may fall inside a block). Outputs, all host memory:
+ *   cu_seqlens_q[num_seqs+1], cu_seqlens_k[num_seqs+1]: prefix sums of end-start and end;
+ *   *max_seqlen_q, *max_seqlen_k;
+ *   slot_mapping[total_q], positions[total_q] (int64): for each computed position p of
+ *     each sequence in order, slot = table[p / bs] * bs + p % bs and p itself;
+ *   block_tables[num_seqs * table_width]: each table copied and padded with -1.
+ * Inputs: block tables are ragged, sequence b's ids are
+ *   block_table_flat[block_table_offsets[b] .. block_table_offsets[b+1]-1].
+ * slot_capacity / positions may be 0 / NULL to skip those outputs' size check / output.
+ * Errors: PKV_ERR_INVALID if a table holds fewer than ceil(end / bs) ids, if a table is
+ * longer than table_width, if total_q exceeds slot_capacity, or on negative counts.
+ * -------------------------------------------------------------------------------------*/
+int pkv_prefill_metadata(int32_t num_seqs, const int32_t* num_cached, const int32_t* num_scheduled,
+                         const int32_t* block_table_flat, const int64_t* block_table_offsets,
+                         int32_t block_size, int32_t table_width,
+                         int32_t* cu_seqlens_q, int32_t* cu_seqlens_k,
+                         int32_t* max_seqlen_q, int32_t* max_seqlen_k,
+                         int32_t* slot_mapping, int64_t slot_capacity, int64_t* positions,
+                         int32_t* block_tables);
+
+/* pkv_decode_metadata - [P1] ModelRunner.prepare_decode, Sequence.last_block_num_tokens;
+ * pinned by [P2]'s decode continuation of the same worked example.
+ * Sequence b has seq_lens[b] = len(seq) >= 1 tokens, the newest one being computed:
+ *   slot_mapping[b] = last table entry * bs + last_block_num_tokens - 1,
+ *   context_lens[b] = seq_lens[b], positions[b] = seq_lens[b] - 1 (int64, may be NULL),
+ *   block_tables[num_seqs * table_width] padded with -1.
+ * Errors: PKV_ERR_INVALID unless every table holds exactly ceil(len / bs) ids (so its last
+ * entry is the newest token's block) and fits table_width. All pointers are host memory. */
+int pkv_decode_metadata(int32_t num_seqs, const int32_t* seq_lens,
+                        const int32_t* block_table_flat, const int64_t* block_table_offsets,
+                        int32_t block_size, int32_t table_width,
+                        int32_t* slot_mapping, int32_t* context_lens, int64_t* positions,
+                        int32_t* block_tables);
+
+/* ------------------------------------------------------------------------------------
+ * store_kvcache - [P1] store_kvcache / store_kvcache_kernel; [P2] 请求执行 – run model.
+ * For every token t < num_tokens with s = slot_mapping[t] != -1, copies the Hkv*D elements
+ * of key row t into k_cache slot s and those of value row t into v_cache slot s, bit for bit.
+ *   key, value   device, [num_tokens, Hkv, D] with token stride *_token_stride elements,
+ *                head stride D and unit element stride (a view into a fused qkv buffer works).
+ *   k_cache, v_cache  device, [num_slots, Hkv * D] (= [num_blocks, bs, Hkv, D] flattened).
+ *   slot_mapping device int32 [num_tokens]; -1 = skip (padding or a prefix-cache hit).
+ *   dtype        PKV_F32 or PKV_BF16 (key, value and the caches share it).
+ * Preconditions: non-negative slots are unique within the call (the engine hands each
+ * token its own slot); a slot >= num_slots or < -1 is skipped and nothing is written for it.
+ * num_tokens == 0 is a no-op. Any token stride works; 16-byte aligned rows take the
+ * vector path. Errors: PKV_ERR_INVALID (null pointers, negative sizes, token stride
+ * smaller than Hkv*D), PKV_ERR_UNSUPPORTED (dtype), PKV_ERR_HIP.
+ * -------------------------------------------------------------------------------------*/
+int store_kvcache(const void* key, int64_t key_token_stride,
+                  const void* value, int64_t value_token_stride,
+                  void* k_cache, void* v_cache, int64_t num_slots,
+                  const int32_t* slot_mapping, int32_t num_tokens,
+                  int32_t num_kv_heads, int32_t head_dim, pkv_dtype_t dtype,
+                  hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Decode attention - [P1] Attention.forward (decode branch, flash_attn_with_kvcache with
+ * cache_seqlens = context_lens and a block table); [P1] prepare_decode for the meaning of
+ * context_lens (len(seq), the newest token included: its K/V is stored before attention).
+ *
+ * For sequence b with n = context_lens[b] and every q head h (kv head g = h / G):
+ *   out[b,h,:] = sum_{j<n} softmax_j(scale * <q[b,h,:], K_b[j,g,:]>) V_b[j,g,:]
+ * where K_b[j] is k_cache[block_tables[b * max_blocks_per_seq + j / bs], j % bs].
+ * The keys are split into partitions of `partition_size` tokens; each partition's
+ * (max, sum, weighted V) is combined exactly afterwards (split-K softmax).
+ *   out          device [num_seqs, Hq, D], dtype
+ *   q            device [num_seqs, Hq, D], dtype, contiguous
+ *   k_cache, v_cache  device [num_blocks, bs, Hkv, D], dtype
+ *   block_tables device int32 [num_seqs, max_blocks_per_seq]; entries at or past
+ *                ceil(n / bs) are never read (padding -1 or stale ids are fine).
+ *   context_lens device int32 [num_seqs]; 0 gives a zero output row without reading memory.
+ *   partition_size  keys per partition, a multiple of 64 in [64, 1024]; 0 = library default.
+ *   workspace    device scratch of at least paged_attn_decode_workspace_bytes(...) bytes,
+ *                owned by the caller; no initial contents needed; the call uses it until
+ *                the stream reaches the end of the call.
+ * Preconditions: n <= max_blocks_per_seq * bs (larger n is clamped to that); table entries
+ * below ceil(n / bs) lie in [0, num_blocks) - an entry outside it is not dereferenced and
+ * turns that sequence's output row into NaN.
+ * Supported: dtype PKV_F32 or PKV_BF16; D in {64, 128}; G in {1, 2, 4, 8}; bs a power of
+ * two >= 16. Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.
+ * -------------------------------------------------------------------------------------*/
+size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                         int32_t max_blocks_per_seq, int32_t block_size,
+                                         int32_t partition_size);
+
+int paged_attn_decode(void* out, const void* q,
+                      const void* k_cache, const void* v_cache, int32_t num_blocks,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, float scale, pkv_dtype_t dtype,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Varlen causal prefill - [P1] Attention.forward (prefill branch, flash_attn_varlen_func
+ * with block_table, causal=True); [P1] prepare_prefill for cu_seqlens; [P2] 请求执行 –
+ * 输入序列预处理与context构建 for prefix-cache hits (keys cover more tokens than queries).
+ *
+ * Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (Lq of them) and
+ * Lk = cu_seqlens_k[b+1] - cu_seqlens_k[b] keys read through its block table, Lk >= Lq.
+ * Query i of the sequence sits at position Lk - Lq + i and attends keys 0 .. Lk - Lq + i
+ * (causal, aligned at the bottom right, so cached prefix tokens are visible to all).
+ *   out, q       device [total_q, Hq, D] bf16, contiguous (packed sequences)
+ *   k_cache, v_cache  device [num_blocks, bs, Hkv, D] bf16 (the new tokens already stored)
+ *   block_tables device int32 [num_seqs, max_blocks_per_seq]
+ *   cu_seqlens_q, cu_seqlens_k  device int32 [num_seqs + 1]
+ *   max_seqlen_q host int: an upper bound of every Lq (sizes the launch, as in the
+ *                engine's Context); max_seqlen_k is accepted for the same interface.
+ *   causal       must be 1 (the engine always attends causally).
+ * Preconditions: cu_seqlens_q[num_seqs] == total_q; Lq <= max_seqlen_q (rows past it are
+ * left unwritten); Lk >= Lq; Lk <= max_blocks_per_seq * bs (larger Lk is clamped); table
+ * entries below ceil(Lk / bs) lie in [0, num_blocks) - an entry outside it is not
+ * dereferenced and turns that sequence's output rows into NaN.
+ * Supported: bf16 only (fp32 accumulation); D in {64, 128}; G in {1, 2, 4, 8}; bs a power
+ * of two >= 16. Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.
+ * -------------------------------------------------------------------------------------*/
+int paged_attn_prefill_varlen(void* out, const void* q,
+                              const void* k_cache, const void* v_cache, int32_t num_blocks,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t num_seqs, int32_t total_q,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, float scale, int32_t causal,
+                              pkv_dtype_t dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGED_KV_H_ */

@@ -1,0 +1,24 @@
+"""Paged-attention hot path for AMD Instinct MI355X (gfx950).
+
+The compute lives in libpaged_kv.so (hand-written HIP kernels behind a C ABI, declared in
+include/paged_kv.h). This package is the thin Python binding over it.
+"""
+from ._binding import (  # noqa: F401
+    PKV_BF16,
+    PKV_F32,
+    PagedKVError,
+    load_library,
+    paged_attn_decode,
+    paged_attn_decode_workspace_bytes,
+    paged_attn_prefill_varlen,
+    pkv_decode_metadata,
+    pkv_prefill_metadata,
+    pkv_status_string,
+    store_kvcache,
+)
+
+__all__ = [
+    "PKV_BF16", "PKV_F32", "PagedKVError", "load_library", "paged_attn_decode",
+    "paged_attn_decode_workspace_bytes", "paged_attn_prefill_varlen", "pkv_decode_metadata",
+    "pkv_prefill_metadata", "pkv_status_string", "store_kvcache",
+]

@@ -1,0 +1,267 @@
+// C ABI of the paged-attention library: argument validation, host metadata, launches.
+// The operations and their sources are documented in include/paged_kv.h.
+#include <limits.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+#include "paged_kv.h"
+
+namespace {
+
+bool pow2_at_least_16(int32_t v) { return v >= 16 && (v & (v - 1)) == 0; }
+bool supported_group(int32_t heads, int32_t kv_heads) {
+  if (heads <= 0 || kv_heads <= 0 || heads % kv_heads) return false;
+  const int32_t g = heads / kv_heads;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int decode_parts(int32_t max_blocks_per_seq, int32_t block_size, int32_t partition,
+                 int32_t* part_out, int64_t* max_parts_out) {
+  const int32_t part = partition == 0 ? pkv::kDecodeDefaultPartition : partition;
+  if (part < 64 || part > pkv::kDecodeMaxPartition || part % 64) return PKV_ERR_INVALID;
+  const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+  if (cap > INT32_MAX) return PKV_ERR_INVALID;
+  *part_out = part;
+  *max_parts_out = ceil_div(cap, part);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PKV_ERR_WORKSPACE: return "workspace too small";
+    case PKV_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+// ------------------------------------------------------------------------- host metadata
+int pkv_prefill_metadata(int32_t num_seqs, const int32_t* num_cached, const int32_t* num_scheduled,
+                         const int32_t* block_table_flat, const int64_t* block_table_offsets,
+                         int32_t block_size, int32_t table_width,
+                         int32_t* cu_seqlens_q, int32_t* cu_seqlens_k,
+                         int32_t* max_seqlen_q, int32_t* max_seqlen_k,
+                         int32_t* slot_mapping, int64_t slot_capacity, int64_t* positions,
+                         int32_t* block_tables) {
+  if (num_seqs < 0 || block_size <= 0 || table_width < 0 || slot_capacity < 0) return PKV_ERR_INVALID;
+  if (!cu_seqlens_q || !cu_seqlens_k || !max_seqlen_q || !max_seqlen_k) return PKV_ERR_INVALID;
+  if (num_seqs > 0 && (!num_cached || !num_scheduled || !block_table_offsets)) return PKV_ERR_INVALID;
+  // validation pass: nothing is written on error
+  int64_t total_q = 0, total_k = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t start = num_cached[b], sched = num_scheduled[b];
+    const int64_t have = block_table_offsets[b + 1] - block_table_offsets[b];
+    if (start < 0 || sched < 0 || have < 0 || have > table_width) return PKV_ERR_INVALID;
+    const int64_t end = start + sched;
+    if (have < ceil_div(end, block_size)) return PKV_ERR_INVALID;
+    if (have > 0 && !block_table_flat) return PKV_ERR_INVALID;
+    total_q += sched;
+    total_k += end;
+    for (int64_t i = 0; i < have; ++i) {
+      const int64_t id = block_table_flat[block_table_offsets[b] + i];
+      if (id < 0 || (id + 1) * (int64_t)block_size - 1 > INT32_MAX) return PKV_ERR_INVALID;
+    }
+  }
+  if (total_q > INT32_MAX || total_k > INT32_MAX || total_q > slot_capacity) return PKV_ERR_INVALID;
+  if (total_q > 0 && !slot_mapping) return PKV_ERR_INVALID;
+  if (num_seqs > 0 && table_width > 0 && !block_tables) return PKV_ERR_INVALID;
+
+  int32_t mq = 0, mk = 0;
+  int64_t n = 0;
+  cu_seqlens_q[0] = 0;
+  cu_seqlens_k[0] = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t start = num_cached[b];
+    const int32_t seqlen_q = num_scheduled[b];
+    const int32_t end = start + seqlen_q;  // = seqlen_k
+    const int32_t* table = block_table_flat + block_table_offsets[b];
+    const int64_t have = block_table_offsets[b + 1] - block_table_offsets[b];
+    cu_seqlens_q[b + 1] = cu_seqlens_q[b] + seqlen_q;
+    cu_seqlens_k[b + 1] = cu_seqlens_k[b] + end;
+    if (seqlen_q > mq) mq = seqlen_q;
+    if (end > mk) mk = end;
+    // walk the blocks that overlap [start, end); each contributes a run of consecutive slots
+    for (int32_t i = start / block_size; i * (int64_t)block_size < end; ++i) {
+      const int32_t first_pos = i * block_size;
+      const int32_t lo = start > first_pos ? start : first_pos;
+      const int32_t hi = end < first_pos + block_size ? end : first_pos + block_size;
+      const int32_t base = table[i] * block_size - first_pos;
+      for (int32_t p = lo; p < hi; ++p, ++n) {
+        slot_mapping[n] = base + p;
+        if (positions) positions[n] = p;
+      }
+    }
+    if (block_tables)
+      for (int32_t i = 0; i < table_width; ++i)
+        block_tables[(int64_t)b * table_width + i] = i < have ? table[i] : -1;
+  }
+  *max_seqlen_q = mq;
+  *max_seqlen_k = mk;
+  return PKV_OK;
+}
+
+int pkv_decode_metadata(int32_t num_seqs, const int32_t* seq_lens,
+                        const int32_t* block_table_flat, const int64_t* block_table_offsets,
+                        int32_t block_size, int32_t table_width,
+                        int32_t* slot_mapping, int32_t* context_lens, int64_t* positions,
+                        int32_t* block_tables) {
+  if (num_seqs < 0 || block_size <= 0 || table_width < 0) return PKV_ERR_INVALID;
+  if (num_seqs == 0) return PKV_OK;
+  if (!seq_lens || !block_table_flat || !block_table_offsets || !slot_mapping || !context_lens)
+    return PKV_ERR_INVALID;
+  if (table_width > 0 && !block_tables) return PKV_ERR_INVALID;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t len = seq_lens[b];
+    const int64_t have = block_table_offsets[b + 1] - block_table_offsets[b];
+    if (len < 1 || have != ceil_div(len, block_size) || have > table_width) return PKV_ERR_INVALID;
+    const int64_t last = block_table_flat[block_table_offsets[b + 1] - 1];
+    if (last < 0 || (last + 1) * (int64_t)block_size - 1 > INT32_MAX) return PKV_ERR_INVALID;
+  }
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t len = seq_lens[b];
+    const int32_t* table = block_table_flat + block_table_offsets[b];
+    const int32_t num_blocks = (int32_t)(block_table_offsets[b + 1] - block_table_offsets[b]);
+    const int32_t last_block_num_tokens = len - (num_blocks - 1) * block_size;
+    slot_mapping[b] = table[num_blocks - 1] * block_size + last_block_num_tokens - 1;
+    context_lens[b] = len;
+    if (positions) positions[b] = len - 1;
+    for (int32_t i = 0; i < table_width; ++i)
+      block_tables[(int64_t)b * table_width + i] = i < num_blocks ? table[i] : -1;
+  }
+  return PKV_OK;
+}
+
+// ------------------------------------------------------------------------- store
+int store_kvcache(const void* key, int64_t key_token_stride, const void* value,
+                  int64_t value_token_stride, void* k_cache, void* v_cache, int64_t num_slots,
+                  const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                  int32_t head_dim, pkv_dtype_t dtype, hipStream_t stream) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_slots < 0 || num_kv_heads <= 0 || head_dim <= 0) return PKV_ERR_INVALID;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (row > INT32_MAX) return PKV_ERR_INVALID;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_INVALID;
+  if (key_token_stride < row || value_token_stride < row) return PKV_ERR_INVALID;
+  const int rc = pkv::launch_store_kvcache(key, key_token_stride, value, value_token_stride,
+                                           k_cache, v_cache, num_slots, slot_mapping, num_tokens,
+                                           (int32_t)row, dtype == PKV_BF16 ? 2 : 4, stream);
+  return rc == 0 ? PKV_OK : PKV_ERR_HIP;
+}
+
+// ------------------------------------------------------------------------- decode
+size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                         int32_t max_blocks_per_seq, int32_t block_size,
+                                         int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+      block_size <= 0)
+    return 0;
+  int32_t part;
+  int64_t max_parts;
+  if (decode_parts(max_blocks_per_seq, block_size, partition_size, &part, &max_parts) != PKV_OK)
+    return 0;
+  if (max_parts <= 1) return 0;
+  return (size_t)num_seqs * num_heads * max_parts * (head_dim + 2) * sizeof(float);
+}
+
+int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                      pkv_dtype_t dtype, int32_t partition_size, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID;
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return PKV_ERR_INVALID;
+  if (!pow2_at_least_16(block_size)) return PKV_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (!supported_group(num_heads, num_kv_heads)) return PKV_ERR_UNSUPPORTED;
+  if (num_kv_heads > 65535 || num_seqs > 65535) return PKV_ERR_UNSUPPORTED;
+  int32_t part;
+  int64_t max_parts;
+  if (decode_parts(max_blocks_per_seq, block_size, partition_size, &part, &max_parts) != PKV_OK)
+    return PKV_ERR_INVALID;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_INVALID;
+  const size_t need = paged_attn_decode_workspace_bytes(num_seqs, num_heads, head_dim,
+                                                        max_blocks_per_seq, block_size,
+                                                        partition_size);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  pkv::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_blocks = num_blocks;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.scale = scale;
+  a.bf16 = dtype == PKV_BF16;
+  a.partition = part;
+  a.max_parts = (int32_t)max_parts;
+  a.ws_o = (float*)workspace;
+  a.ws_ml = need ? (float*)workspace + (size_t)num_seqs * num_heads * max_parts * head_dim : nullptr;
+  const int rc = pkv::launch_decode(a, stream);
+  return rc == 0 ? PKV_OK : (rc == -2 ? PKV_ERR_UNSUPPORTED : PKV_ERR_HIP);
+}
+
+// ------------------------------------------------------------------------- prefill
+int paged_attn_prefill_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              int32_t num_blocks, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t total_q,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              float scale, int32_t causal, pkv_dtype_t dtype,
+                              hipStream_t stream) {
+  (void)max_seqlen_k;
+  if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (causal != 1) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || num_blocks < 0 || max_blocks_per_seq <= 0)
+    return PKV_ERR_INVALID;
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return PKV_ERR_INVALID;
+  if (!pow2_at_least_16(block_size)) return PKV_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (!supported_group(num_heads, num_kv_heads)) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PKV_ERR_INVALID;
+  if (num_seqs > 65535 || ceil_div(max_seqlen_q, 64) > 65535) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens_q || !cu_seqlens_k)
+    return PKV_ERR_INVALID;
+  pkv::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_blocks = num_blocks;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.cu_seqlens_k = cu_seqlens_k;
+  a.num_seqs = num_seqs;
+  a.max_seqlen_q = max_seqlen_q;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.scale = scale;
+  const int rc = pkv::launch_prefill(a, stream);
+  return rc == 0 ? PKV_OK : (rc == -2 ? PKV_ERR_UNSUPPORTED : PKV_ERR_HIP);
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal launchers behind the C ABI (argument validation happens in api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kDecodeDefaultPartition = 256;
+constexpr int kDecodeMaxPartition = 1024;
+
+int launch_store_kvcache(const void* key, int64_t key_stride, const void* value,
+                         int64_t value_stride, void* k_cache, void* v_cache, int64_t num_slots,
+                         const int32_t* slot_mapping, int32_t num_tokens, int32_t row_elems,
+                         int32_t elem_bytes, hipStream_t stream);
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  int32_t num_blocks;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* context_lens;
+  int32_t num_seqs, num_heads, num_kv_heads, head_dim, block_size;
+  float scale;
+  int32_t bf16;             // 1 = bf16, 0 = fp32
+  int32_t partition;        // keys per partition
+  int32_t max_parts;        // partitions of the longest possible context
+  float* ws_o;              // [num_seqs, Hq, max_parts, D]
+  float* ws_ml;             // [num_seqs, Hq, max_parts, 2]
+};
+int launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  int32_t num_blocks;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int32_t num_seqs, max_seqlen_q;
+  int32_t num_heads, num_kv_heads, head_dim, block_size;
+  float scale;
+};
+int launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace pkv

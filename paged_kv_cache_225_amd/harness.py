@@ -1,0 +1,129 @@
+"""Device-side driver of one engine step, built only on the library's entry points.
+
+``DeviceStep(w)`` takes a seeded workload (see the ``workloads`` package), allocates the
+paged pool on the GPU poisoned with NaN (as the engine's ``torch.empty`` pool holds
+arbitrary bits), makes the resident tokens resident with the library's own metadata and
+``store_kvcache``, and prepares the step's inputs. ``step()`` then runs the hot path:
+``store_kvcache`` of the new tokens followed by ``paged_attn_decode`` or
+``paged_attn_prefill_varlen``. Host metadata is built by the library's host calls.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _binding as B
+
+
+def _to_device(raw: np.ndarray, dtype: str, device) -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(raw, dtype=np.float32)).to(device)
+
+
+def _i32(a, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+def poison_fill_(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype == torch.bfloat16:
+        t.view(torch.int16).fill_(0x7FC0)
+    else:
+        t.view(torch.int32).fill_(0x7FC00000)
+    return t
+
+
+class DeviceStep:
+    def __init__(self, w, device="cuda", fill=None, partition_size=0, table_width=None):
+        self.w = w
+        self.device = torch.device(device)
+        self.partition_size = partition_size
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+        self.k_cache = torch.empty(shape, dtype=tdt, device=self.device)
+        self.v_cache = torch.empty(shape, dtype=tdt, device=self.device)
+        if fill is None:
+            poison_fill_(self.k_cache)
+            poison_fill_(self.v_cache)
+        else:
+            self.k_cache.fill_(fill)
+            self.v_cache.fill_(fill)
+        self._make_resident()
+        self.table_width = w.max_table_len() if table_width is None else table_width
+        self._prepare_step()
+
+    # resident tokens: the common prefix once, then each sequence's private resident range
+    def _make_resident(self):
+        w = self.w
+        segs_cached, segs_sched, segs_tables, ks, vs = [], [], [], [], []
+        n_pre = len(w.prefix_block_ids) * w.block_size
+        if n_pre:
+            segs_cached.append(0)
+            segs_sched.append(n_pre)
+            segs_tables.append(w.prefix_block_ids)
+            ks.append(w.prefix_k)
+            vs.append(w.prefix_v)
+        for b, lo, hi in w.resident_segments():
+            segs_cached.append(lo)
+            segs_sched.append(hi - lo)
+            segs_tables.append(w.block_tables[b])
+            k, v = w.seq_token_rows(b, lo, hi)
+            ks.append(k)
+            vs.append(v)
+        if not ks:
+            return
+        md = B.pkv_prefill_metadata(segs_cached, segs_sched, segs_tables, w.block_size)
+        k = _to_device(np.concatenate(ks), w.dtype, self.device)
+        v = _to_device(np.concatenate(vs), w.dtype, self.device)
+        B.store_kvcache(k, v, self.k_cache, self.v_cache, _i32(md["slot_mapping"], self.device))
+        torch.cuda.synchronize(self.device)
+
+    def _prepare_step(self):
+        w, dev = self.w, self.device
+        if w.kind == "decode":
+            md = B.pkv_decode_metadata(w.seq_lens, w.block_tables, w.block_size, self.table_width)
+            self.context_lens = _i32(md["context_lens"], dev)
+        else:
+            md = B.pkv_prefill_metadata(w.num_cached, w.q_lens, w.block_tables, w.block_size,
+                                        self.table_width)
+            self.cu_seqlens_q = _i32(md["cu_seqlens_q"], dev)
+            self.cu_seqlens_k = _i32(md["cu_seqlens_k"], dev)
+            self.max_seqlen_q = md["max_seqlen_q"]
+            self.max_seqlen_k = md["max_seqlen_k"]
+        self.md = md
+        self.slot_mapping = _i32(md["slot_mapping"], dev)
+        self.block_tables = _i32(md["block_tables"].reshape(w.num_seqs, -1), dev)
+        nk, nv = w.new_tokens()
+        self.new_k = _to_device(nk, w.dtype, dev)
+        self.new_v = _to_device(nv, w.dtype, dev)
+        self.q = _to_device(w.q, w.dtype, dev)
+        self.out = torch.empty_like(self.q)
+        if w.kind == "decode":
+            nbytes = B.paged_attn_decode_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim,
+                                                         self.block_tables.shape[1], w.block_size,
+                                                         self.partition_size)
+            self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+    def store(self, stream=None):
+        B.store_kvcache(self.new_k, self.new_v, self.k_cache, self.v_cache, self.slot_mapping,
+                        stream=stream)
+
+    def attend(self, stream=None):
+        w = self.w
+        if w.kind == "decode":
+            B.paged_attn_decode(self.out, self.q, self.k_cache, self.v_cache, self.block_tables,
+                                self.context_lens, w.scale, workspace=self.workspace,
+                                partition_size=self.partition_size, stream=stream)
+        else:
+            B.paged_attn_prefill_varlen(self.out, self.q, self.k_cache, self.v_cache,
+                                        self.block_tables, self.cu_seqlens_q, self.cu_seqlens_k,
+                                        self.max_seqlen_q, self.max_seqlen_k, w.scale, stream=stream)
+
+    def step(self, stream=None):
+        self.store(stream)
+        self.attend(stream)
+        return self.out
+
+    def out_f64(self) -> np.ndarray:
+        o = self.out.float().cpu().numpy() if self.out.dtype == torch.bfloat16 else self.out.cpu().numpy()
+        return o.astype(np.float64)
