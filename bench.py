@@ -194,6 +194,21 @@ def cpu_baseline(w, budget_s):
                       f"+ fp64 attention over all 64 sequences), {t_total:.1f} s"}
 
 
+def copy_calibration(torch, reps):
+    """A plain copy of a known size: FETCH_SIZE / WRITE_SIZE per dispatch should read 1 GiB."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "reps": reps,
+                      "copy_gbs": 2 * n / dt / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +219,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
+                    help="copy: run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -215,6 +232,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.mode == "copy":
+        copy_calibration(torch, args.steps)
+        return
     print("bench: decode headline", file=sys.stderr, flush=True)
     head = bench_decode_headline(torch, args)
     w = head.pop("w")
