@@ -119,23 +119,29 @@ int store_kvcache(const void* key, int64_t key_token_stride,
  * For sequence b with n = context_lens[b] and every q head h (kv head g = h / G):
  *   out[b,h,:] = sum_{j<n} softmax_j(scale * <q[b,h,:], K_b[j,g,:]>) V_b[j,g,:]
  * where K_b[j] is k_cache[block_tables[b * max_blocks_per_seq + j / bs], j % bs].
- * The keys are split into partitions of `partition_size` tokens; each partition's
- * (max, sum, weighted V) is combined exactly afterwards (split-K softmax).
+ * The (sequence, kv head) key segments are laid end to end and every wavefront takes an equal
+ * contiguous share of them (never fewer than `partition_size` keys); a segment cut between
+ * shares is merged exactly afterwards from per-share (max, sum, weighted V) partials (split-K
+ * softmax), so the result does not depend on how the keys were split beyond rounding.
  *   out          device [num_seqs, Hq, D], dtype
  *   q            device [num_seqs, Hq, D], dtype, contiguous
  *   k_cache, v_cache  device [num_blocks, bs, Hkv, D], dtype
  *   block_tables device int32 [num_seqs, max_blocks_per_seq]; entries at or past
  *                ceil(n / bs) are never read (padding -1 or stale ids are fine).
  *   context_lens device int32 [num_seqs]; 0 gives a zero output row without reading memory.
- *   partition_size  keys per partition, a multiple of 64 in [64, 1024]; 0 = library default.
- *   workspace    device scratch of at least paged_attn_decode_workspace_bytes(...) bytes,
- *                owned by the caller; no initial contents needed; the call uses it until
- *                the stream reaches the end of the call.
+ *   partition_size  smallest share of keys per wavefront, a multiple of 64 in [64, 1024];
+ *                0 = library default (256). It also sizes the workspace.
+ *   workspace    device scratch of at least paged_attn_decode_workspace_bytes(...) bytes
+ *                (same num_seqs, heads, head_dim, max_blocks_per_seq, block_size and
+ *                partition_size), owned by the caller; no initial contents needed; in use
+ *                until the stream passes the end of the call, so calls that overlap on
+ *                different streams need different workspaces.
  * Preconditions: n <= max_blocks_per_seq * bs (larger n is clamped to that); table entries
  * below ceil(n / bs) lie in [0, num_blocks) - an entry outside it is not dereferenced and
  * turns that sequence's output row into NaN.
  * Supported: dtype PKV_F32 or PKV_BF16; D in {64, 128}; G in {1, 2, 4, 8}; bs a power of
- * two >= 16. Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.
+ * two >= 16; num_seqs <= 16383 and num_seqs * max_blocks_per_seq * bs * Hkv < 2^31.
+ * Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.
  * -------------------------------------------------------------------------------------*/
 size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                          int32_t max_blocks_per_seq, int32_t block_size,

@@ -1,6 +1,7 @@
 // C ABI of the paged-attention library: argument validation, host metadata, launches.
 // The operations and their sources are documented in include/paged_kv.h.
 #include <limits.h>
+#include <stdlib.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
@@ -25,7 +26,7 @@ int decode_parts(int32_t max_blocks_per_seq, int32_t block_size, int32_t partiti
   const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
   if (cap > INT32_MAX) return PKV_ERR_INVALID;
   *part_out = part;
-  *max_parts_out = ceil_div(cap, part);
+  *max_parts_out = ceil_div(cap, part) + 1;  // pieces a segment can be cut into
   return PKV_OK;
 }
 
@@ -169,8 +170,9 @@ size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, in
   int64_t max_parts;
   if (decode_parts(max_blocks_per_seq, block_size, partition_size, &part, &max_parts) != PKV_OK)
     return 0;
-  if (max_parts <= 1) return 0;
-  return (size_t)num_seqs * num_heads * max_parts * (head_dim + 2) * sizeof(float);
+  const size_t partials = (size_t)num_seqs * num_heads * max_parts * (head_dim + 2) * sizeof(float);
+  const size_t meta = ((size_t)num_seqs + 2) * sizeof(int32_t);
+  return partials + meta;
 }
 
 int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -185,7 +187,10 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
   if (!pow2_at_least_16(block_size)) return PKV_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (!supported_group(num_heads, num_kv_heads)) return PKV_ERR_UNSUPPORTED;
-  if (num_kv_heads > 65535 || num_seqs > 65535) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs > 16383) return PKV_ERR_UNSUPPORTED;  // the context prefix lives in 64 KiB of LDS
+  // the kernels number every key row of every (sequence, kv head) with an int32
+  if ((int64_t)num_seqs * max_blocks_per_seq * block_size * num_kv_heads > INT32_MAX)
+    return PKV_ERR_UNSUPPORTED;
   int32_t part;
   int64_t max_parts;
   if (decode_parts(max_blocks_per_seq, block_size, partition_size, &part, &max_parts) != PKV_OK)
@@ -195,7 +200,7 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
   const size_t need = paged_attn_decode_workspace_bytes(num_seqs, num_heads, head_dim,
                                                         max_blocks_per_seq, block_size,
                                                         partition_size);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
   pkv::DecodeArgs a;
   a.out = out;
   a.q = q;
@@ -215,7 +220,13 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
   a.partition = part;
   a.max_parts = (int32_t)max_parts;
   a.ws_o = (float*)workspace;
-  a.ws_ml = need ? (float*)workspace + (size_t)num_seqs * num_heads * max_parts * head_dim : nullptr;
+  a.max_workgroups = pkv::kDecodeDefaultWorkgroups;
+  if (const char* env = getenv("PKV_DECODE_WORKGROUPS")) {
+    const int v = atoi(env);
+    if (v > 0) a.max_workgroups = v;
+  }
+  a.ws_ml = (float*)workspace + (size_t)num_seqs * num_heads * max_parts * head_dim;
+  a.ws_meta = (int32_t*)(a.ws_ml + (size_t)num_seqs * num_heads * max_parts * 2);
   const int rc = pkv::launch_decode(a, stream);
   return rc == 0 ? PKV_OK : (rc == -2 ? PKV_ERR_UNSUPPORTED : PKV_ERR_HIP);
 }

@@ -4,21 +4,28 @@
 // 源码逐段精读": one query per sequence attends every cached key of the sequence (context
 // length = len(seq), newest token included), K/V gathered through the block table.
 //
-// Work unit of decode_partial_kernel: (partition p, kv head g, sequence b). The unit reads
-// the K and V rows of its keys for kv head g only and serves all G query heads of the
-// group, so each K/V byte is read from HBM once. Inside a workgroup (4 wavefronts):
-//   * a K or V row of one head (D elements) is spread over LPR lanes, 16 bytes per lane,
-//     so one wavefront load instruction reads RPI whole rows;
-//   * pass 1 loads K in chunks of kNI instructions per wave (kNI loads in flight per lane),
-//     forms the G dot products per row with a DPP reduction inside the row's lanes and
-//     leaves the scaled scores (log2 units) in LDS;
-//   * pass 2 takes the partition's max and sum of exp2 over the LDS scores;
-//   * pass 3 loads V the same way and accumulates the weighted rows in registers, then
-//     reduces across the rows of a wavefront (shuffles) and across wavefronts (LDS).
-// A sequence with a single partition writes its output directly; otherwise the unit
-// writes (max, sum, weighted V) for each head and decode_reduce_kernel combines them:
+// Work split (stream-K over the keys). Lay the work out as one line of key rows: for every
+// sequence b in order and every kv head g, a segment of n_b = context_lens[b] keys. Every
+// wavefront of the grid takes an equal, contiguous share S of that line (S is computed on
+// the device from context_lens, never below `min_keys`), so each wavefront moves the same
+// number of K/V bytes however the context lengths are spread. A share can start or end
+// inside a segment and can cover several short segments; the part of a segment inside one
+// share is a piece. A piece reads the K and V rows of its keys for head g only and serves
+// all G query heads of the group, so each K/V byte leaves HBM once.
+//
+// Inside a wavefront a row of one head (D elements) is spread over LPR lanes, 16 bytes per
+// lane, so one load instruction covers RPI rows; a chunk is NI such instructions (CH keys).
+// The wavefront walks its share chunk by chunk with a two-deep register pipeline: the K and
+// V loads of the next chunk are issued before the current chunk is computed, across piece
+// boundaries too. Per chunk, the G dot products of each row (v_dot2_f32_bf16 on packed bf16,
+// or fp32 FMAs) are summed over the row's lanes with DPP, and every row group (the lanes
+// sharing one row slot) updates its own online-softmax state in log2 units:
+//   m' = max(m, chunk max);  l, o scaled by 2^(m - m');  l += 2^(s - m');  o += 2^(s - m') v.
+// At the end of a piece the row groups are merged with shuffles. A piece that is a whole
+// segment writes the normalised output row; otherwise it writes (m, l, o) per query head
+// into its slot, and decode_combine_kernel merges the slots of each (sequence, head):
 //   M = max_p m_p, L = sum_p 2^(m_p - M) l_p, out = sum_p 2^(m_p - M) o_p / L.
-// Keys past the context length are never loaded: block-table padding and the unused
+// Keys past the context length are never loaded, so block-table padding and the unused
 // (possibly NaN) slots of a sequence's last block are not touched.
 #include <math.h>
 
@@ -27,222 +34,367 @@
 
 namespace pkv {
 
-constexpr int kNI = 8;  // load instructions per wavefront per chunk
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void decode_partial_kernel(
+__device__ __forceinline__ int clamp_ctx(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
+
+// One chunk of a wavefront's share: keys [k, k + cnt) of segment (b, g).
+struct Chunk {
+  int x;          // position of the chunk's first key on the line
+  int b, g, k, cnt;
+  int seg_start;  // line position of key 0 of the segment
+  int n;          // segment length (context length of b)
+  bool piece_start, piece_end;
+};
+
+template <typename T, int D, int G, int NI>
+__global__ __launch_bounds__(256) void decode_stream_kernel(
     T* __restrict__ out, const T* __restrict__ q, const T* __restrict__ k_cache,
     const T* __restrict__ v_cache, int32_t num_blocks, const int32_t* __restrict__ block_tables,
-    int32_t bt_stride, const int32_t* __restrict__ context_lens, int32_t num_kv_heads,
-    int32_t bs_log2, float scale_log2e, int32_t part, int32_t max_parts,
-    float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+    int32_t bt_stride, const int32_t* __restrict__ context_lens, int32_t num_seqs,
+    int32_t num_kv_heads, int32_t bs_log2, float scale_log2e, int32_t min_keys,
+    int32_t max_pieces, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    int32_t* __restrict__ ws_meta) {
   using E = Elem<T>;
+  constexpr bool kBF16 = E::kBytes == 2;
   constexpr int EPL = E::kPerChunk;  // elements per 16-byte lane chunk
   constexpr int LPR = D / EPL;       // lanes per row
-  constexpr int RPI = 64 / LPR;      // rows per wavefront instruction
-  constexpr int CH = 4 * RPI * kNI;  // keys per chunk (workgroup)
+  constexpr int RPI = 64 / LPR;      // rows per load instruction
+  constexpr int CH = RPI * NI;       // keys per chunk
   static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "row must tile a wavefront");
 
-  __shared__ float s_sc[G][kDecodeMaxPartition];
-  __shared__ float s_red[4][G];
-  __shared__ float s_o[4][G][D];
+  extern __shared__ int32_t s_cum[];  // [num_seqs + 1]: prefix sums of the context lengths
 
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int Hq = num_kv_heads * G;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane % LPR, rsub = lane / LPR;
-
-  int n = context_lens[b];
   const int cap = bt_stride << bs_log2;
-  n = n < 0 ? 0 : (n > cap ? cap : n);
-  const int nparts = (n + part - 1) / part;
-  T* out_bg = out + ((int64_t)b * Hq + (int64_t)g * G) * D;
-  if (n == 0) {
-    if (p == 0)
-      for (int i = threadIdx.x; i < G * D; i += 256) E::store(out_bg + i, 0.f);
-    return;
+  if (threadIdx.x < 64) {
+    int carry = 0;
+    for (int base = 0; base < num_seqs; base += 64) {
+      const int b = base + threadIdx.x;
+      int v = b < num_seqs ? clamp_ctx(context_lens[b], cap) : 0;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off);
+        if ((int)threadIdx.x >= off) v += t;
+      }
+      if (b < num_seqs) s_cum[b + 1] = carry + v;
+      carry += __shfl(v, 63);
+    }
+    if (threadIdx.x == 0) s_cum[0] = 0;
   }
-  if (p >= nparts) return;
-  const int k0 = p * part;
-  const int nk = min(part, n - k0);
+  __syncthreads();
 
-  const int64_t row_elems = (int64_t)num_kv_heads * D;
-  const int64_t head_off = (int64_t)g * D + sub * EPL;
-  const int32_t* bt = block_tables + (int64_t)b * bt_stride;
+  const int Hkv = num_kv_heads;
+  const int Hq = Hkv * G;
+  const int total = Hkv * s_cum[num_seqs];
+  const int n_waves = gridDim.x * 4;
+  int S = (total + n_waves - 1) / n_waves;
+  S = S < min_keys ? min_keys : S;
+  if (blockIdx.x == 0) {  // publish the split for the combine kernel
+    for (int i = threadIdx.x; i <= num_seqs; i += 256) ws_meta[1 + i] = s_cum[i];
+    if (threadIdx.x == 0) ws_meta[0] = S;
+  }
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int w = blockIdx.x * 4 + wave;
+  const int64_t xb = (int64_t)w * S;
+  if (xb >= total) return;
+  const int x_begin = (int)xb;
+  const int x_end = (int)min((int64_t)total, xb + S);
+  const int sub = lane % LPR, rsub = lane / LPR;
+  const int64_t row_elems = (int64_t)Hkv * D;
   const int bs_mask = (1 << bs_log2) - 1;
 
-  float qf[G][EPL];
+  auto locate = [&](int x, Chunk& c) {
+    int lo = 0, hi = num_seqs - 1;  // last b whose segments start at or before x
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (Hkv * s_cum[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    c.b = lo;
+    c.n = s_cum[lo + 1] - s_cum[lo];
+    const int off = x - Hkv * s_cum[lo];
+    c.g = off / c.n;
+    c.k = off - c.g * c.n;
+    c.seg_start = x - c.k;
+  };
+  auto finish_desc = [&](Chunk& c, bool starts_piece) {
+    const int seg_end = c.seg_start + c.n;
+    c.cnt = min(CH, min(seg_end, x_end) - c.x);
+    c.piece_start = starts_piece;
+    c.piece_end = (c.x + c.cnt == seg_end) || (c.x + c.cnt == x_end);
+  };
+  auto next_of = [&](const Chunk& c, Chunk& nx) {
+    nx.x = c.x + c.cnt;
+    if (!c.piece_end) {  // same segment
+      nx.b = c.b; nx.g = c.g; nx.n = c.n; nx.seg_start = c.seg_start; nx.k = c.k + c.cnt;
+      finish_desc(nx, false);
+    } else {
+      locate(nx.x, nx);
+      finish_desc(nx, true);
+    }
+  };
+  // A window of 64 consecutive block-table entries of one sequence, one per lane; every kv
+  // head of the sequence uses the same table, so the window is reloaded only when the
+  // sequence changes or a chunk runs past it.
+  int bt_b = -1, bt_base = 0, bt_reg = -1;
+  auto issue = [&](const Chunk& c, u32x4_t* kr, u32x4_t* vr) {
+    const int first = c.k >> bs_log2, last = (c.k + c.cnt - 1) >> bs_log2;
+    if (c.b != bt_b || first < bt_base || last >= bt_base + 64) {
+      bt_b = c.b;
+      bt_base = first;
+      bt_reg = bt_base + lane < bt_stride ? block_tables[(int64_t)c.b * bt_stride + bt_base + lane] : -1;
+    }
+    const int64_t head_off = (int64_t)c.g * D + sub * EPL;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-    E::unpack(load16(q + ((int64_t)b * Hq + g * G + h) * D + sub * EPL), qf[h]);
+    for (int i = 0; i < NI; ++i) {
+      const int r = i * RPI + rsub;
+      const int j = c.k + r;
+      const int blk = __shfl(bt_reg, min((j >> bs_log2) - bt_base, 63));
+      kr[i] = u32x4_t{0u, 0u, 0u, 0u};
+      vr[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (r < c.cnt) {
+        if ((unsigned)blk < (unsigned)num_blocks) {
+          const int64_t off = (((int64_t)blk << bs_log2) + (j & bs_mask)) * row_elems + head_off;
+          kr[i] = load16(k_cache + off);
+          vr[i] = load16(v_cache + off);
+        } else {
+          kr[i] = E::nan_chunk();
+          vr[i] = E::nan_chunk();
+        }
+      }
+    }
+  };
+  auto load_q = [&](const Chunk& c, u32x4_t* qw) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      qw[h] = load16(q + ((int64_t)c.b * Hq + c.g * G + h) * D + sub * EPL);
+  };
 
-  auto load_rows = [&](const T* cache, int c0, u32x4_t* r) {
+  float m[G], l[G], o[G][EPL];
+  auto reset = [&]() {
 #pragma unroll
-    for (int i = 0; i < kNI; ++i) {
-      const int kl = c0 + (wave * kNI + i) * RPI + rsub;
-      r[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (kl < nk) {
-        const int j = k0 + kl;
-        const int blk = bt[j >> bs_log2];
-        if ((unsigned)blk < (unsigned)num_blocks)
-          r[i] = load16(cache + (((int64_t)blk << bs_log2) + (j & bs_mask)) * row_elems + head_off);
-        else
-          r[i] = E::nan_chunk();
+    for (int h = 0; h < G; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
+    }
+  };
+
+  auto compute = [&](const Chunk& c, const u32x4_t* kr, const u32x4_t* vr, const u32x4_t* qw) {
+    float qf[G][EPL];
+    if constexpr (!kBF16) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) E::unpack(qw[h], qf[h]);
+    }
+    float s[NI][G];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float kf[EPL];
+      if constexpr (!kBF16) E::unpack(kr[i], kf);
+      const bool valid = i * RPI + rsub < c.cnt;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float acc = 0.f;
+        if constexpr (kBF16) {
+          acc = dot2_bf16(kr[i].x, qw[h].x, acc);
+          acc = dot2_bf16(kr[i].y, qw[h].y, acc);
+          acc = dot2_bf16(kr[i].z, qw[h].z, acc);
+          acc = dot2_bf16(kr[i].w, qw[h].w, acc);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc = fmaf(qf[h][e], kf[e], acc);
+        }
+        acc = group_sum<LPR>(acc) * scale_log2e;
+        s[i][h] = valid ? acc : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mc = s[0][h];
+#pragma unroll
+      for (int i = 1; i < NI; ++i) mc = fmaxf(mc, s[i][h]);
+      const float m_new = fmaxf(m[h], mc);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m[h] - m_use);
+      m[h] = m_new;
+      l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) s[i][h] = __builtin_amdgcn_exp2f(s[i][h] - m_use);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float vf[EPL];
+      E::unpack(vr[i], vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        l[h] += s[i][h];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(s[i][h], vf[e], o[h][e]);
       }
     }
   };
 
-  // ---- pass 1: scores -------------------------------------------------------------------
-  for (int c0 = 0; c0 < nk; c0 += CH) {
-    u32x4_t kr[kNI];
-    load_rows(k_cache, c0, kr);
+  auto finalize = [&](const Chunk& c, int piece_x0) {
+    // merge the row groups (lanes with equal `sub`)
 #pragma unroll
-    for (int i = 0; i < kNI; ++i) {
-      float kf[EPL];
-      E::unpack(kr[i], kf);
-      const int kl = c0 + (wave * kNI + i) * RPI + rsub;
+    for (int h = 0; h < G; ++h) {
+      float mall = m[h];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float s = 0.f;
+      for (int msk = LPR; msk < 64; msk <<= 1) mall = fmaxf(mall, __shfl_xor(mall, msk));
+      const float muse = mall == -INFINITY ? 0.f : mall;
+      const float sc = __builtin_amdgcn_exp2f(m[h] - muse);
+      float lt = l[h] * sc;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) s = fmaf(qf[h][e], kf[e], s);
-        s = group_sum<LPR>(s);
-        if (sub == 0 && kl < nk) s_sc[h][kl] = s * scale_log2e;
+      for (int msk = LPR; msk < 64; msk <<= 1) lt += __shfl_xor(lt, msk);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float v = o[h][e] * sc;
+#pragma unroll
+        for (int msk = LPR; msk < 64; msk <<= 1) v += __shfl_xor(v, msk);
+        o[h][e] = v;
       }
+      m[h] = mall;
+      l[h] = lt;
     }
-  }
-  __syncthreads();
-
-  // ---- pass 2: partition max and sum of exp2 -------------------------------------------
-  float m[G], l[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float mx = -INFINITY;
-    for (int t = threadIdx.x; t < nk; t += 256) mx = fmaxf(mx, s_sc[h][t]);
-    mx = group_max<64>(mx);
-    if (lane == 0) s_red[wave][h] = mx;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-    m[h] = fmaxf(fmaxf(s_red[0][h], s_red[1][h]), fmaxf(s_red[2][h], s_red[3][h]));
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float sum = 0.f;
-    for (int t = threadIdx.x; t < nk; t += 256) {
-      const float e = __builtin_amdgcn_exp2f(s_sc[h][t] - m[h]);
-      s_sc[h][t] = e;
-      sum += e;
-    }
-    sum = group_sum<64>(sum);
-    if (lane == 0) s_red[wave][h] = sum;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < G; ++h) l[h] = (s_red[0][h] + s_red[1][h]) + (s_red[2][h] + s_red[3][h]);
-
-  // ---- pass 3: weighted V ----------------------------------------------------------------
-  float o[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
-  for (int c0 = 0; c0 < nk; c0 += CH) {
-    u32x4_t vr[kNI];
-    load_rows(v_cache, c0, vr);
-#pragma unroll
-    for (int i = 0; i < kNI; ++i) {
-      const int kl = c0 + (wave * kNI + i) * RPI + rsub;
-      if (kl < nk) {
-        float vf[EPL];
-        E::unpack(vr[i], vf);
+    if (rsub == 0) {
+      const bool whole = piece_x0 == c.seg_start && c.x + c.cnt == c.seg_start + c.n;
+      if (whole) {
+        T* dst0 = out + ((int64_t)c.b * Hq + c.g * G) * D + sub * EPL;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float pw = s_sc[h][kl];
+          const float inv = 1.f / l[h];
+          T* dst = dst0 + h * D;
+          if constexpr (kBF16) {
+            u32x4_t wv;
+            wv.x = pack_bf16x2(o[h][0] * inv, o[h][1] * inv);
+            wv.y = pack_bf16x2(o[h][2] * inv, o[h][3] * inv);
+            wv.z = pack_bf16x2(o[h][4] * inv, o[h][5] * inv);
+            wv.w = pack_bf16x2(o[h][6] * inv, o[h][7] * inv);
+            store16(dst, wv);
+          } else {
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(pw, vf[e], o[h][e]);
+            for (int e = 0; e < EPL; ++e) E::store(dst + e, o[h][e] * inv);
+          }
+        }
+      } else {
+        const int piece = w - c.seg_start / S;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const int64_t slot = ((int64_t)c.b * Hq + c.g * G + h) * max_pieces + piece;
+          float* dst = ws_o + slot * D + sub * EPL;
+#pragma unroll
+          for (int e = 0; e < EPL; e += 4)
+            store16(dst + e, u32x4_t{__float_as_uint(o[h][e]), __float_as_uint(o[h][e + 1]),
+                                     __float_as_uint(o[h][e + 2]), __float_as_uint(o[h][e + 3])});
+          if (sub == 0) {
+            ws_ml[2 * slot] = m[h];
+            ws_ml[2 * slot + 1] = l[h];
+          }
         }
       }
     }
-  }
-  // rows of one wavefront -> lanes 0..LPR-1
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e)
-#pragma unroll
-      for (int msk = LPR; msk < 64; msk <<= 1) o[h][e] += __shfl_xor(o[h][e], msk);
-  if (rsub == 0)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s_o[wave][h][sub * EPL + e] = o[h][e];
-  __syncthreads();
+    reset();
+  };
 
-  for (int i = threadIdx.x; i < G * D; i += 256) {
-    const int h = i / D, d = i % D;
-    const float acc = (s_o[0][h][d] + s_o[1][h][d]) + (s_o[2][h][d] + s_o[3][h][d]);
-    if (nparts == 1) {
-      E::store(out_bg + i, acc / l[h]);
-    } else {
-      const int64_t u = ((int64_t)b * Hq + g * G + h) * max_parts + p;
-      ws_o[u * D + d] = acc;
-      if (d == 0) {
-        ws_ml[2 * u] = m[h];
-        ws_ml[2 * u + 1] = l[h];
-      }
+  // ---- the pipeline: two register buffers, next chunk issued before the current computes --
+  u32x4_t kA[NI], vA[NI], kB[NI], vB[NI];
+  u32x4_t qc[G], qn[G];
+  Chunk cur, nxt;
+  cur.x = x_begin;
+  locate(x_begin, cur);
+  finish_desc(cur, true);
+  load_q(cur, qc);
+  issue(cur, kA, vA);
+  reset();
+  int piece_x0 = x_begin;
+
+  auto half_step = [&](u32x4_t* kc, u32x4_t* vc, u32x4_t* kn, u32x4_t* vn) -> bool {
+    const bool has_next = cur.x + cur.cnt < x_end;
+    if (has_next) {
+      next_of(cur, nxt);
+      if (nxt.piece_start) load_q(nxt, qn);
+      issue(nxt, kn, vn);
     }
+    compute(cur, kc, vc, qc);
+    if (cur.piece_end) finalize(cur, piece_x0);
+    if (!has_next) return false;
+    if (nxt.piece_start) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) qc[h] = qn[h];
+      piece_x0 = nxt.x;
+    }
+    cur = nxt;
+    return true;
+  };
+  while (half_step(kA, vA, kB, vB) && half_step(kB, vB, kA, vA)) {
   }
 }
 
+// Merges the partial slots of every (sequence, query head) whose segment was split.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_reduce_kernel(
+__global__ __launch_bounds__(D) void decode_combine_kernel(
     T* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t cap, int32_t Hq,
-    int32_t part, int32_t max_parts, const float* __restrict__ ws_o,
-    const float* __restrict__ ws_ml) {
+    int32_t Hkv, int32_t max_pieces, const float* __restrict__ ws_o,
+    const float* __restrict__ ws_ml, const int32_t* __restrict__ ws_meta) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  int n = context_lens[b];
-  n = n < 0 ? 0 : (n > cap ? cap : n);
-  const int nparts = (n + part - 1) / part;
-  if (nparts <= 1) return;
-  const int64_t base = ((int64_t)b * Hq + h) * max_parts;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ws_ml[2 * (base + p)]);
-  float L = 0.f, acc = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float w = __builtin_amdgcn_exp2f(ws_ml[2 * (base + p)] - M);
-    L = fmaf(w, ws_ml[2 * (base + p) + 1], L);
-    acc = fmaf(w, ws_o[(base + p) * D + d], acc);
+  const int n = clamp_ctx(context_lens[b], cap);
+  T* dst = out + ((int64_t)b * Hq + h) * D + d;
+  if (n == 0) {
+    Elem<T>::store(dst, 0.f);
+    return;
   }
-  Elem<T>::store(out + ((int64_t)b * Hq + h) * D + d, acc / L);
+  const int S = ws_meta[0];
+  const int g = h / (Hq / Hkv);
+  const int seg_start = Hkv * ws_meta[1 + b] + g * n;
+  const int np = (seg_start + n - 1) / S - seg_start / S + 1;
+  if (np == 1) return;  // written by the stream kernel
+  const int64_t base = ((int64_t)b * Hq + h) * max_pieces;
+  float M = -INFINITY;
+  for (int p = 0; p < np; ++p) M = fmaxf(M, ws_ml[2 * (base + p)]);
+  float L = 0.f, acc = 0.f;
+  for (int p = 0; p < np; ++p) {
+    const float wgt = __builtin_amdgcn_exp2f(ws_ml[2 * (base + p)] - M);
+    L = fmaf(wgt, ws_ml[2 * (base + p) + 1], L);
+    acc = fmaf(wgt, ws_o[(base + p) * D + d], acc);
+  }
+  Elem<T>::store(dst, acc / L);
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int NI>
 static int run_decode(const DecodeArgs& a, hipStream_t stream) {
   const int bs_log2 = __builtin_ctz((unsigned)a.block_size);
   const float c = a.scale * kLog2e;
-  dim3 grid1(a.max_parts, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_partial_kernel<T, D, G>), grid1, dim3(256), 0, stream, (T*)a.out,
-                     (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache, a.num_blocks,
-                     a.block_tables, a.max_blocks_per_seq, a.context_lens, a.num_kv_heads,
-                     bs_log2, c, a.partition, a.max_parts, a.ws_o, a.ws_ml);
-  if (a.max_parts > 1) {
-    dim3 grid2(a.num_heads, a.num_seqs);
-    hipLaunchKernelGGL((decode_reduce_kernel<T, D>), grid2, dim3(D), 0, stream, (T*)a.out,
-                       a.context_lens, a.max_blocks_per_seq * a.block_size, a.num_heads,
-                       a.partition, a.max_parts, a.ws_o, a.ws_ml);
-  }
+  const int64_t cap = (int64_t)a.max_blocks_per_seq * a.block_size;
+  const int64_t upper = (int64_t)a.num_seqs * cap * a.num_kv_heads;  // keys at full contexts
+  int64_t blocks = (upper + 4LL * a.partition - 1) / (4LL * a.partition);
+  if (blocks > a.max_workgroups) blocks = a.max_workgroups;
+  if (blocks < 1) blocks = 1;
+  const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
+  hipLaunchKernelGGL((decode_stream_kernel<T, D, G, NI>), dim3((unsigned)blocks), dim3(256), lds,
+                     stream, (T*)a.out, (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache,
+                     a.num_blocks, a.block_tables, a.max_blocks_per_seq, a.context_lens,
+                     a.num_seqs, a.num_kv_heads, bs_log2, c, a.partition, a.max_parts, a.ws_o,
+                     a.ws_ml, a.ws_meta);
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.num_heads, a.num_seqs), dim3(D), 0,
+                     stream, (T*)a.out, a.context_lens, (int32_t)cap, a.num_heads,
+                     a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 template <typename T, int D>
 static int dispatch_g(const DecodeArgs& a, hipStream_t s) {
   switch (a.num_heads / a.num_kv_heads) {
-    case 1: return run_decode<T, D, 1>(a, s);
-    case 2: return run_decode<T, D, 2>(a, s);
-    case 4: return run_decode<T, D, 4>(a, s);
-    case 8: return run_decode<T, D, 8>(a, s);
+    case 1: return run_decode<T, D, 1, 8>(a, s);
+    case 2: return run_decode<T, D, 2, 8>(a, s);
+    case 4: return run_decode<T, D, 4, 4>(a, s);
+    case 8: return run_decode<T, D, 8, 2>(a, s);
     default: return -2;
   }
 }

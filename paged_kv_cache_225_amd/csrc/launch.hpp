@@ -6,8 +6,9 @@
 
 namespace pkv {
 
-constexpr int kDecodeDefaultPartition = 256;
+constexpr int kDecodeDefaultPartition = 256;   // smallest share of keys per wavefront
 constexpr int kDecodeMaxPartition = 1024;
+constexpr int kDecodeDefaultWorkgroups = 512;  // 4 wavefronts each: 2 per SIMD on 256 CUs
 
 int launch_store_kvcache(const void* key, int64_t key_stride, const void* value,
                          int64_t value_stride, void* k_cache, void* v_cache, int64_t num_slots,
@@ -26,10 +27,12 @@ struct DecodeArgs {
   int32_t num_seqs, num_heads, num_kv_heads, head_dim, block_size;
   float scale;
   int32_t bf16;             // 1 = bf16, 0 = fp32
-  int32_t partition;        // keys per partition
-  int32_t max_parts;        // partitions of the longest possible context
+  int32_t partition;        // smallest share of keys per wavefront (min_keys)
+  int32_t max_parts;        // partial slots per (sequence, head): ceil(cap / partition) + 1
   float* ws_o;              // [num_seqs, Hq, max_parts, D]
   float* ws_ml;             // [num_seqs, Hq, max_parts, 2]
+  int32_t* ws_meta;         // [num_seqs + 2]: the share size, then the context prefix sums
+  int32_t max_workgroups;   // cap of the decode grid (4 wavefronts each)
 };
 int launch_decode(const DecodeArgs& a, hipStream_t stream);
 

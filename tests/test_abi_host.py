@@ -161,7 +161,12 @@ def test_store_argument_validation():
 
 
 def test_workspace_query():
-    assert B.paged_attn_decode_workspace_bytes(4, 16, 128, 1, 256, 256) == 0   # one partition
-    n = B.paged_attn_decode_workspace_bytes(4, 16, 128, 16, 256, 256)
-    assert n == 4 * 16 * 16 * (128 + 2) * 4
-    assert B.paged_attn_decode_workspace_bytes(4, 16, 128, 16, 256, 64) == 4 * 16 * 64 * 130 * 4
+    # partial slots per (sequence, q head): ceil(cap / partition) + 1, then num_seqs + 2 ints
+    def expect(B, Hq, D, W, bs, part):
+        cap = W * bs
+        slots = -(-cap // part) + 1
+        return B * Hq * slots * (D + 2) * 4 + (B + 2) * 4
+    assert B.paged_attn_decode_workspace_bytes(4, 16, 128, 1, 256, 256) == expect(4, 16, 128, 1, 256, 256)
+    assert B.paged_attn_decode_workspace_bytes(4, 16, 128, 16, 256, 256) == expect(4, 16, 128, 16, 256, 256)
+    assert B.paged_attn_decode_workspace_bytes(4, 16, 128, 16, 256, 0) == expect(4, 16, 128, 16, 256, 256)
+    assert B.paged_attn_decode_workspace_bytes(4, 16, 128, 16, 256, 100) == 0     # invalid partition
