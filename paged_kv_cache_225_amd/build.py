@@ -7,6 +7,7 @@ Run as ``python -m paged_kv_cache_225_amd.build``.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import ctypes
 import glob
 import os
 import shutil
@@ -56,6 +57,11 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # every symbol must resolve: a kernel whose host launch stub went missing shows up here
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW)
+    except OSError as e:
+        raise RuntimeError(f"built library does not load: {e}") from e
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH} from {len(srcs)} sources", flush=True)

@@ -10,18 +10,22 @@
 // Units are numbered from the end of each sequence so the longest rows (most keys) are
 // dispatched first. Each of the 4 wavefronts owns 16 query positions x GH heads.
 //
-// Per key tile of 64 keys, staged through LDS (K row-major, V transposed):
-//   S^T = K Q^T   with v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 dims of K (one 16-byte LDS
-//                 read per lane), B = Q^T held in registers for the whole unit. The result
-//                 leaves lane l with 4 keys of query column l % 16, so the running max, the
-//                 exp2 and the running sum stay per lane (two cross-lane steps per tile for
-//                 the max only).
-//   O^T += V^T P^T  with the same MFMA: the B operand is the lane's own probabilities
-//                 (bf16), the A operand reads V^T from LDS with the key order that matches
-//                 the lane's registers. O^T accumulates in registers, one query per lane.
-// The softmax is the online form: m' = max(m, tile max), O and l scaled by 2^(m - m').
-// Scores enter exp2 as s * scale * log2(e). Keys past Lk are zero-filled in LDS (never
-// read from the cache), so padding entries and unused NaN slots cannot reach an MFMA.
+// Key tiles of 64 keys go from HBM straight into LDS with global_load_lds_dwordx4 (no
+// register staging), double-buffered: the loads of tile t+1 are issued right after the
+// barrier that publishes tile t, and the block-table entries of tile t+2 are fetched
+// behind them, so one barrier per tile is all the synchronisation there is. In LDS a K
+// row keeps its 16-byte chunks XOR-swizzled by the row index and a V row its 32-byte
+// chunks, so the MFMA operand reads below hit distinct banks.
+//   S^T = K Q^T   v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 dims of K (one ds_read_b128
+//                 per lane), B = Q^T held in registers for the whole unit. Lane l ends with
+//                 4 keys of query column l % 16, so the running max, exp2 and the running sum
+//                 stay per lane (two cross-lane steps per tile for the max).
+//   O^T += V^T P^T  same MFMA: B = the lane's own probabilities (bf16); A = V^T, read with
+//                 ds_read_b64_tr_b16, which hands every lane four consecutive keys of one
+//                 head dimension - the key order the lane's probabilities are in.
+// The softmax is the online form in log2 units: m' = max(m, tile max), O and l scaled by
+// 2^(m - m') (skipped when no column's max moved). Keys past Lk are zero-filled in LDS and
+// never read from the cache, so padding entries and unused NaN slots cannot reach an MFMA.
 #include <math.h>
 
 #include "common.hpp"
@@ -32,25 +36,39 @@ namespace pkv {
 constexpr int kBK = 64;  // keys per tile
 constexpr int kBQ = 64;  // query positions per workgroup
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
 __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane. The builtin
+// exists only for the device target; the host pass of this file must not see it (it would
+// drop the kernels' launch stubs), so the body is compiled for the device pass only.
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+#endif
+}
+
 template <int D, int GH>
-__global__ __launch_bounds__(256) void prefill_kernel(
+__global__ __launch_bounds__(256, 2) void prefill_kernel(
     __bf16* __restrict__ out, const __bf16* __restrict__ q, const __bf16* __restrict__ k_cache,
     const __bf16* __restrict__ v_cache, int32_t num_blocks,
     const int32_t* __restrict__ block_tables, int32_t bt_stride,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_heads,
     int32_t num_kv_heads, int32_t bs_log2, float scale_log2e) {
-  constexpr int KS = D / 32;             // k-steps of the QK^T product
-  constexpr int DT = D / 16;             // 16-row tiles of O^T
-  constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
-  constexpr int NC = kBK * CPR / 256;    // chunks per thread per tile
-  constexpr int KSTR = D + 8;            // K tile row stride (elements)
-  constexpr int VSTR = kBK + 4;          // V^T tile row stride (elements)
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[kBK * KSTR];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[D * VSTR];
+  constexpr int KS = D / 32;                 // k-steps of the QK^T product
+  constexpr int DT = D / 16;                 // 16-row tiles of O^T
+  constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
+  constexpr int RPL = 64 / CPR;              // rows per direct-load instruction
+  constexpr int NL = kBK / RPL / 4;          // direct-load instructions per wave per tile
+  constexpr int ROWB = D * 2;                // bytes per K/V row in LDS
+  constexpr int TILEB = kBK * ROWB;          // bytes per K (or V) tile
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][TILEB];  // [buffer][K=0,V=1]
 
   const int hg = blockIdx.x, b = blockIdx.y, t = blockIdx.z;
   const int G = num_heads / num_kv_heads;
@@ -90,6 +108,47 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       qb[nt][s] = __builtin_bit_cast(bf16x8_t, v);
     }
 
+  // ---- direct HBM -> LDS tile loads -------------------------------------------------------
+  // Instruction i of this wave fills LDS bytes [(wave*NL + i) * 1024, +1024) of a tile: rows
+  // RPL * (wave*NL + i) + lane / CPR, slot lane % CPR. K slot s of row r holds chunk
+  // s ^ (r % CPR); V slot s holds chunk 2 * ((s/2) ^ (r % (CPR/2))) + s % 2 (32-byte swizzle).
+  int lrow[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) lrow[i] = RPL * (wave * NL + i) + lane / CPR;
+  const int slot = lane % CPR;
+  int kchunk[NL], vchunk[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    kchunk[i] = slot ^ (lrow[i] % CPR);
+    vchunk[i] = 2 * ((slot >> 1) ^ (lrow[i] % (CPR / 2))) + (slot & 1);
+  }
+  int nblk[NL];  // block ids of this lane's rows for a tile two steps ahead
+  auto fetch_blocks = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int j = kt * kBK + lrow[i];
+      nblk[i] = (kt < n_kt && j < Lk) ? bt[j >> bs_log2] : -1;
+    }
+  };
+  auto issue_tile = [&](int kt, int buf, const int* blk) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int j = kt * kBK + lrow[i];
+      char* kdst = &lds[buf][0][(wave * NL + i) * 1024];
+      char* vdst = &lds[buf][1][(wave * NL + i) * 1024];
+      if (j < Lk && (unsigned)blk[i] < (unsigned)num_blocks) {
+        const int64_t rowoff = (((int64_t)blk[i] << bs_log2) + (j & bs_mask)) * row_elems + (int64_t)g * D;
+        load_lds16(k_cache + rowoff + 8 * kchunk[i], kdst);
+        load_lds16(v_cache + rowoff + 8 * vchunk[i], vdst);
+      } else {
+        // past the sequence: zeros; a bad block id: NaN (poisons only this sequence's rows)
+        const u32x4_t fill = j < Lk ? Elem<__bf16>::nan_chunk() : u32x4_t{0u, 0u, 0u, 0u};
+        store16(kdst + 16 * lane, fill);
+        store16(vdst + 16 * lane, fill);
+      }
+    }
+  };
+
   f32x4_t oacc[DT][GH];
 #pragma unroll
   for (int i = 0; i < DT; ++i)
@@ -102,50 +161,27 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     l_run[nt] = 0.f;
   }
 
-  u32x4_t kreg[NC], vreg[NC];
-  auto load_tile = [&](int kt) {
+  int cblk[NL];
+  if (n_kt > 0) {
+    fetch_blocks(0);
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int u = i * 256 + tid;
-      const int key = u / CPR, c = u % CPR;
-      const int j = kt * kBK + key;
-      kreg[i] = u32x4_t{0u, 0u, 0u, 0u};
-      vreg[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (j < Lk) {
-        const int blk = bt[j >> bs_log2];
-        if ((unsigned)blk < (unsigned)num_blocks) {
-          const int64_t o = (((int64_t)blk << bs_log2) + (j & bs_mask)) * row_elems +
-                            (int64_t)g * D + 8 * c;
-          kreg[i] = load16(k_cache + o);
-          vreg[i] = load16(v_cache + o);
-        } else {
-          kreg[i] = Elem<__bf16>::nan_chunk();
-          vreg[i] = Elem<__bf16>::nan_chunk();
-        }
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int u = i * 256 + tid;
-      const int key = u / CPR, c = u % CPR;
-      store16(&Ks[key * KSTR + 8 * c], kreg[i]);
-      const uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(8 * c + 2 * e) * VSTR + key] = __builtin_bit_cast(__bf16, (uint16_t)(w[e] & 0xffffu));
-        Vt[(8 * c + 2 * e + 1) * VSTR + key] = __builtin_bit_cast(__bf16, (uint16_t)(w[e] >> 16));
-      }
-    }
-  };
-
-  if (n_kt > 0) load_tile(0);
+    for (int i = 0; i < NL; ++i) cblk[i] = nblk[i];
+    wait_vmem();
+    issue_tile(0, 0, cblk);
+    fetch_blocks(1);
+  }
   for (int kt = 0; kt < n_kt; ++kt) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+    const int buf = kt & 1;
+    wait_vmem();          // this wave's part of tile kt (and the block ids of tile kt+1)
+    __syncthreads();      // every wave's part; every wave is done with the other buffer
+    if (kt + 1 < n_kt) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) cblk[i] = nblk[i];
+      issue_tile(kt + 1, buf ^ 1, cblk);
+      fetch_blocks(kt + 2);
+    }
+    const char* Kt = lds[buf][0];
+    const char* Vt = lds[buf][1];
 
     // S^T = K Q^T : sacc[mt][nt][r] = score of key kt*64 + 16 mt + 4 quad + r, column col
     f32x4_t sacc[4][GH];
@@ -157,16 +193,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&Ks[(16 * mt + col) * KSTR + 32 * s + 8 * quad]);
+        const int r = 16 * mt + col;
+        const int c = (4 * s + quad) ^ (r % CPR);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kt + r * ROWB + 16 * c);
 #pragma unroll
         for (int nt = 0; nt < GH; ++nt) sacc[mt][nt] = mfma16(a, qb[nt][s], sacc[mt][nt]);
       }
 
     const bool need_mask = kt * kBK + kBK - 1 > wave_min_pos;
     bf16x8_t pb[2][GH];
+    bool moved = false;
+    float alpha[GH];
 #pragma unroll
     for (int nt = 0; nt < GH; ++nt) {
-      float sv[4][4];
       float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -176,53 +215,69 @@ __global__ __launch_bounds__(256) void prefill_kernel(
           if (need_mask) {
             const int j = kt * kBK + 16 * mt + 4 * quad + r;
             s = (j <= pos) ? s : -INFINITY;
+            sacc[mt][nt][r] = s;
           }
-          sv[mt][r] = s;
           mx = fmaxf(mx, s);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run[nt], mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f((m_run[nt] - m_use) * scale_log2e);
+      alpha[nt] = __builtin_amdgcn_exp2f((m_run[nt] - m_use) * scale_log2e);
+      moved |= m_new != m_run[nt];
       const float mc = m_use * scale_log2e;
       float psum = 0.f;
+      float pv[4][4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sv[mt][r], scale_log2e, -mc));
-          sv[mt][r] = e;
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mt][nt][r], scale_log2e, -mc));
+          pv[mt][r] = e;
           psum += e;
         }
-      l_run[nt] = fmaf(alpha, l_run[nt], psum);
+      l_run[nt] = fmaf(alpha[nt], l_run[nt], psum);
       m_run[nt] = m_new;
-#pragma unroll
-      for (int i = 0; i < DT; ++i) oacc[i][nt] *= alpha;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         u32x4_t w;
-        w.x = pack_bf16x2(sv[2 * ks][0], sv[2 * ks][1]);
-        w.y = pack_bf16x2(sv[2 * ks][2], sv[2 * ks][3]);
-        w.z = pack_bf16x2(sv[2 * ks + 1][0], sv[2 * ks + 1][1]);
-        w.w = pack_bf16x2(sv[2 * ks + 1][2], sv[2 * ks + 1][3]);
+        w.x = pack_bf16x2(pv[2 * ks][0], pv[2 * ks][1]);
+        w.y = pack_bf16x2(pv[2 * ks][2], pv[2 * ks][3]);
+        w.z = pack_bf16x2(pv[2 * ks + 1][0], pv[2 * ks + 1][1]);
+        w.w = pack_bf16x2(pv[2 * ks + 1][2], pv[2 * ks + 1][3]);
         pb[ks][nt] = __builtin_bit_cast(bf16x8_t, w);
       }
     }
+    if (__any(moved)) {
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int nt = 0; nt < GH; ++nt) oacc[i][nt] *= alpha[nt];
+    }
 
-    // O^T += V^T P^T ; A operand lane (row d = 16 i + col) holds keys
-    // {32 ks + 4 quad + 0..3} then {32 ks + 16 + 4 quad + 0..3}, matching pb's order.
+    // O^T += V^T P^T ; lane (row d = 16 i + col, group quad) reads keys 32 ks + 4 quad + 0..3
+    // and 32 ks + 16 + 4 quad + 0..3 with two transposing reads. Source lane L of a group
+    // points at key k0 + L / 4, dims 16 i + 4 (L % 4) .. + 3.
 #pragma unroll
     for (int i = 0; i < DT; ++i)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const __bf16* vrow = &Vt[(16 * i + col) * VSTR + 32 * ks + 4 * quad];
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 16);
-        const u32x4_t w = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, w);
+        s16x4_t part[2];
 #pragma unroll
-        for (int nt = 0; nt < GH; ++nt) oacc[i][nt] = mfma16(a, pb[ks][nt], oacc[i][nt]);
+        for (int hf = 0; hf < 2; ++hf) {
+          const int r = 32 * ks + 16 * hf + 4 * quad + (col >> 2);
+          const int c2 = i ^ (r % (CPR / 2));  // 32-byte chunk i, swizzled
+          const char* src = Vt + r * ROWB + 32 * c2 + 8 * (col & 3);
+          part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)src);
+        }
+        u32x4_t w;
+        w.x = __builtin_bit_cast(u32x2_t, part[0]).x;
+        w.y = __builtin_bit_cast(u32x2_t, part[0]).y;
+        w.z = __builtin_bit_cast(u32x2_t, part[1]).x;
+        w.w = __builtin_bit_cast(u32x2_t, part[1]).y;
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, w);
+#pragma unroll
+        for (int nt = 0; nt < GH; ++nt) oacc[i][nt] = mfma16(av, pb[ks][nt], oacc[i][nt]);
       }
   }
 
