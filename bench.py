@@ -221,6 +221,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
                     help="copy: run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--only", choices=["prefill3", "prefill4", "large"], default=None,
+                    help="run one secondary workload alone (for profiler passes)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -234,6 +236,11 @@ def main():
     torch.cuda.set_device(0)
     if args.mode == "copy":
         copy_calibration(torch, args.steps)
+        return
+    if args.only is not None:
+        res = (bench_large_decode(torch, args.iters, 5) if args.only == "large"
+               else bench_prefill(torch, 3 if args.only == "prefill3" else 4, args.iters, 5))
+        print(json.dumps({"only": args.only, **res}), flush=True)
         return
     print("bench: decode headline", file=sys.stderr, flush=True)
     head = bench_decode_headline(torch, args)

@@ -17,10 +17,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Two floats -> packed bf16 pair (round to nearest even; lowers to v_cvt_pk_bf16_f32).
+// Two floats -> packed bf16 pair (round to nearest even; one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  typedef float f32x2_v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_v){lo, hi}, bf16x2_v));
 }
 
 // ---- element traits: a 16-byte lane chunk holds EPL elements ------------------------

@@ -28,6 +28,8 @@
 // never read from the cache, so padding entries and unused NaN slots cannot reach an MFMA.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -43,7 +45,24 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Reductions over the four lanes l, l^16, l^32, l^48 (the 16-lane rows of a wavefront) with
+// v_permlane16_swap / v_permlane32_swap: VALU lane exchanges, no LDS round trip.
+__device__ __forceinline__ float rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left free) through the builtin, so the compiler's own
+// wait placement knows every earlier vector-memory result has landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane. The builtin
 // exists only for the device target; the host pass of this file must not see it (it would
@@ -68,7 +87,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   constexpr int NL = kBK / RPL / 4;          // direct-load instructions per wave per tile
   constexpr int ROWB = D * 2;                // bytes per K/V row in LDS
   constexpr int TILEB = kBK * ROWB;          // bytes per K (or V) tile
-  __shared__ __attribute__((aligned(1024))) char lds[2][2][TILEB];  // [buffer][K=0,V=1]
+  // two buffers as distinct objects: with the tile loop unrolled by two, every LDS read of
+  // one buffer is known not to alias the HBM->LDS loads in flight into the other, so no
+  // wait on those loads is placed before the reads
+  __shared__ __attribute__((aligned(1024))) char lds_a[2][TILEB];  // [K=0,V=1]
+  __shared__ __attribute__((aligned(1024))) char lds_b[2][TILEB];
 
   const int hg = blockIdx.x, b = blockIdx.y, t = blockIdx.z;
   const int G = num_heads / num_kv_heads;
@@ -130,14 +153,34 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       nblk[i] = (kt < n_kt && j < Lk) ? bt[j >> bs_log2] : -1;
     }
   };
-  auto issue_tile = [&](int kt, int buf, const int* blk) {
+  auto issue_tile = [&](int kt, char (*dst)[TILEB], const int* blk) {
+    bool ok[NL];
+    bool all_ok = true;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int j = kt * kBK + lrow[i];
-      char* kdst = &lds[buf][0][(wave * NL + i) * 1024];
-      char* vdst = &lds[buf][1][(wave * NL + i) * 1024];
-      if (j < Lk && (unsigned)blk[i] < (unsigned)num_blocks) {
-        const int64_t rowoff = (((int64_t)blk[i] << bs_log2) + (j & bs_mask)) * row_elems + (int64_t)g * D;
+      ok[i] = j < Lk && (unsigned)blk[i] < (unsigned)num_blocks;
+      all_ok &= ok[i];
+    }
+    if (__all(all_ok)) {  // every row of the tile is a real key: loads only, no branches
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int j = kt * kBK + lrow[i];
+        const int64_t rowoff =
+            (int64_t)((blk[i] << bs_log2) + (j & bs_mask)) * row_elems + (int64_t)g * D;
+        load_lds16(k_cache + rowoff + 8 * kchunk[i], &dst[0][(wave * NL + i) * 1024]);
+        load_lds16(v_cache + rowoff + 8 * vchunk[i], &dst[1][(wave * NL + i) * 1024]);
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int j = kt * kBK + lrow[i];
+      char* kdst = &dst[0][(wave * NL + i) * 1024];
+      char* vdst = &dst[1][(wave * NL + i) * 1024];
+      if (ok[i]) {
+        const int64_t rowoff =
+            (int64_t)((blk[i] << bs_log2) + (j & bs_mask)) * row_elems + (int64_t)g * D;
         load_lds16(k_cache + rowoff + 8 * kchunk[i], kdst);
         load_lds16(v_cache + rowoff + 8 * vchunk[i], vdst);
       } else {
@@ -167,21 +210,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 #pragma unroll
     for (int i = 0; i < NL; ++i) cblk[i] = nblk[i];
     wait_vmem();
-    issue_tile(0, 0, cblk);
+    issue_tile(0, lds_a, cblk);
     fetch_blocks(1);
   }
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
+  auto tile_step = [&](int kt, char (*cur)[TILEB], char (*nxt)[TILEB]) {
     wait_vmem();          // this wave's part of tile kt (and the block ids of tile kt+1)
     __syncthreads();      // every wave's part; every wave is done with the other buffer
     if (kt + 1 < n_kt) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) cblk[i] = nblk[i];
-      issue_tile(kt + 1, buf ^ 1, cblk);
+      issue_tile(kt + 1, nxt, cblk);
       fetch_blocks(kt + 2);
     }
-    const char* Kt = lds[buf][0];
-    const char* Vt = lds[buf][1];
+    const char* Kt = cur[0];
+    const char* Vt = cur[1];
 
     // S^T = K Q^T : sacc[mt][nt][r] = score of key kt*64 + 16 mt + 4 quad + r, column col
     f32x4_t sacc[4][GH];
@@ -200,54 +242,58 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
         for (int nt = 0; nt < GH; ++nt) sacc[mt][nt] = mfma16(a, qb[nt][s], sacc[mt][nt]);
       }
 
-    const bool need_mask = kt * kBK + kBK - 1 > wave_min_pos;
+    // online softmax of the tile; the causal mask only on tiles that cross this wave's diagonal
     bf16x8_t pb[2][GH];
     bool moved = false;
     float alpha[GH];
+    auto softmax = [&](auto masked) {
+      constexpr bool kMask = decltype(masked)::value;
 #pragma unroll
-    for (int nt = 0; nt < GH; ++nt) {
-      float mx = -INFINITY;
+      for (int nt = 0; nt < GH; ++nt) {
+        float mx = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float s = sacc[mt][nt][r];
-          if (need_mask) {
-            const int j = kt * kBK + 16 * mt + 4 * quad + r;
-            s = (j <= pos) ? s : -INFINITY;
-            sacc[mt][nt][r] = s;
+          for (int r = 0; r < 4; ++r) {
+            if constexpr (kMask) {
+              const int j = kt * kBK + 16 * mt + 4 * quad + r;
+              if (j > pos) sacc[mt][nt][r] = -INFINITY;
+            }
+            mx = fmaxf(mx, sacc[mt][nt][r]);
           }
-          mx = fmaxf(mx, s);
+        mx = rows_max(mx);
+        const float m_new = fmaxf(m_run[nt], mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        alpha[nt] = __builtin_amdgcn_exp2f((m_run[nt] - m_use) * scale_log2e);
+        moved |= m_new != m_run[nt];
+        const float mc = m_use * scale_log2e;
+        float psum = 0.f;
+        float pv[4][4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mt][nt][r], scale_log2e, -mc));
+            pv[mt][r] = e;
+            psum += e;
+          }
+        l_run[nt] = fmaf(alpha[nt], l_run[nt], psum);
+        m_run[nt] = m_new;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          u32x4_t w;
+          w.x = pack_bf16x2(pv[2 * ks][0], pv[2 * ks][1]);
+          w.y = pack_bf16x2(pv[2 * ks][2], pv[2 * ks][3]);
+          w.z = pack_bf16x2(pv[2 * ks + 1][0], pv[2 * ks + 1][1]);
+          w.w = pack_bf16x2(pv[2 * ks + 1][2], pv[2 * ks + 1][3]);
+          pb[ks][nt] = __builtin_bit_cast(bf16x8_t, w);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[nt], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      alpha[nt] = __builtin_amdgcn_exp2f((m_run[nt] - m_use) * scale_log2e);
-      moved |= m_new != m_run[nt];
-      const float mc = m_use * scale_log2e;
-      float psum = 0.f;
-      float pv[4][4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mt][nt][r], scale_log2e, -mc));
-          pv[mt][r] = e;
-          psum += e;
-        }
-      l_run[nt] = fmaf(alpha[nt], l_run[nt], psum);
-      m_run[nt] = m_new;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u32x4_t w;
-        w.x = pack_bf16x2(pv[2 * ks][0], pv[2 * ks][1]);
-        w.y = pack_bf16x2(pv[2 * ks][2], pv[2 * ks][3]);
-        w.z = pack_bf16x2(pv[2 * ks + 1][0], pv[2 * ks + 1][1]);
-        w.w = pack_bf16x2(pv[2 * ks + 1][2], pv[2 * ks + 1][3]);
-        pb[ks][nt] = __builtin_bit_cast(bf16x8_t, w);
       }
-    }
+    };
+    if (kt * kBK + kBK - 1 > wave_min_pos)
+      softmax(std::true_type{});
+    else
+      softmax(std::false_type{});
     if (__any(moved)) {
 #pragma unroll
       for (int i = 0; i < DT; ++i)
@@ -259,9 +305,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     // and 32 ks + 16 + 4 quad + 0..3 with two transposing reads. Source lane L of a group
     // points at key k0 + L / 4, dims 16 i + 4 (L % 4) .. + 3.
 #pragma unroll
-    for (int i = 0; i < DT; ++i)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int i = 0; i < DT; ++i) {
         s16x4_t part[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -279,15 +325,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 #pragma unroll
         for (int nt = 0; nt < GH; ++nt) oacc[i][nt] = mfma16(av, pb[ks][nt], oacc[i][nt]);
       }
+  };
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    tile_step(kt, lds_a, lds_b);
+    if (kt + 1 < n_kt) tile_step(kt + 1, lds_b, lds_a);
   }
 
   // normalise and store: lane holds dims 16 i + 4 quad + r of its query column
 #pragma unroll
   for (int nt = 0; nt < GH; ++nt) {
-    float l = l_run[nt];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const float inv = 1.f / l;
+    const float inv = 1.f / rows_sum(l_run[nt]);
     if (row_ok) {
       __bf16* orow = out + ((int64_t)(q_begin + i_row) * num_heads + h0 + nt) * D;
 #pragma unroll
