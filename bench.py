@@ -128,7 +128,7 @@ def bench_decode_headline(torch, args):
         "decode_call_us_p10_p90": [float(np.percentile(dec_ms, 10)) * 1e3,
                                    float(np.percentile(dec_ms, 90)) * 1e3],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": decode_traffic_bytes()},
     }
 
 
@@ -164,6 +164,31 @@ def bench_large_decode(torch, iters, warmup):
             "unique_gbs": uniq / (med * 1e-3) / 1e9, "logical_gbs": logi / (med * 1e-3) / 1e9,
             "frac_hbm_unique": uniq / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "tokens_per_s": w.num_seqs / (med * 1e-3), "shared_hist": w.meta.get("shared_hist")}
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b64_hbm_traffic.json")
+
+
+def decode_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("common.hpp", "launch.hpp", "decode.hip"):
+        with open(os.path.join(ROOT, "paged_kv_cache_225_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def decode_traffic_bytes():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, or None
+    when the decode kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_sources_sha256") != decode_sources_sha256():
+        return None
+    return d.get("traffic_bytes_per_launch")
 
 
 def host_metadata_us(w, reps=20):
