@@ -136,9 +136,9 @@ int store_kvcache(const void* key, int64_t key_token_stride,
  *                partition_size), owned by the caller; no initial contents needed; in use
  *                until the stream passes the end of the call, so calls that overlap on
  *                different streams need different workspaces.
- * Preconditions: n <= max_blocks_per_seq * bs (larger n is clamped to that); table entries
- * below ceil(n / bs) lie in [0, num_blocks) - an entry outside it is not dereferenced and
- * turns that sequence's output row into NaN.
+ * Preconditions: num_blocks >= 1; n <= max_blocks_per_seq * bs (larger n is clamped to
+ * that); table entries below ceil(n / bs) lie in [0, num_blocks) - an entry outside it is
+ * not dereferenced and turns that sequence's output row into NaN.
  * Supported: dtype PKV_F32 or PKV_BF16; D in {64, 128}; G in {1, 2, 4, 8}; bs a power of
  * two >= 16; num_seqs <= 16383 and num_seqs * max_blocks_per_seq * bs * Hkv < 2^31.
  * Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.

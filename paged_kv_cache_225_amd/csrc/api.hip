@@ -182,7 +182,7 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
                       pkv_dtype_t dtype, int32_t partition_size, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
   if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
-  if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID;
+  if (num_seqs < 0 || num_blocks < 1 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID;
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return PKV_ERR_INVALID;
   if (!pow2_at_least_16(block_size)) return PKV_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;

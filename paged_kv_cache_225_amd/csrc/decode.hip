@@ -51,7 +51,7 @@ struct Chunk {
   bool piece_start, piece_end;
 };
 
-template <typename T, int D, int G, int NI>
+template <typename T, int D, int G, int NI, int HPW>
 __global__ __launch_bounds__(256) void decode_stream_kernel(
     T* __restrict__ out, const T* __restrict__ q, const T* __restrict__ k_cache,
     const T* __restrict__ v_cache, int32_t num_blocks, const int32_t* __restrict__ block_tables,
@@ -63,7 +63,11 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   constexpr bool kBF16 = E::kBytes == 2;
   constexpr int EPL = E::kPerChunk;  // elements per 16-byte lane chunk
   constexpr int LPR = D / EPL;       // lanes per row
-  constexpr int RPI = 64 / LPR;      // rows per load instruction
+  // HPW == 0: each wavefront owns a share of the (sequence, kv head) line and one head per
+  // chunk. HPW > 0: each workgroup owns a share of the (sequence) line and its wavefront w
+  // serves kv heads w*HPW .. w*HPW+HPW-1, so the group reads whole token rows together.
+  constexpr int RSTRIDE = (HPW > 0 ? HPW : 1) * LPR;  // lanes between rows of one instruction
+  constexpr int RPI = 64 / RSTRIDE;  // rows (keys) per load instruction
   constexpr int CH = RPI * NI;       // keys per chunk
   static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "row must tile a wavefront");
 
@@ -89,8 +93,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
 
   const int Hkv = num_kv_heads;
   const int Hq = Hkv * G;
-  const int total = Hkv * s_cum[num_seqs];
-  const int n_waves = gridDim.x * 4;
+  const int mult = HPW > 0 ? 1 : Hkv;  // line positions per key of a sequence
+  const int total = mult * s_cum[num_seqs];
+  const int n_waves = HPW > 0 ? gridDim.x : gridDim.x * 4;  // share owners
   int S = (total + n_waves - 1) / n_waves;
   S = S < min_keys ? min_keys : S;
   if (blockIdx.x == 0) {  // publish the split for the combine kernel
@@ -99,12 +104,13 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   }
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int w = blockIdx.x * 4 + wave;
+  const int w = HPW > 0 ? blockIdx.x : blockIdx.x * 4 + wave;  // share owner
   const int64_t xb = (int64_t)w * S;
   if (xb >= total) return;
   const int x_begin = (int)xb;
   const int x_end = (int)min((int64_t)total, xb + S);
-  const int sub = lane % LPR, rsub = lane / LPR;
+  const int sub = lane % LPR, rsub = lane / RSTRIDE;
+  const int g_lane = HPW > 0 ? wave * HPW + (lane / LPR) % HPW : 0;  // this lane's kv head
   const int64_t row_elems = (int64_t)Hkv * D;
   const int bs_mask = (1 << bs_log2) - 1;
 
@@ -112,13 +118,13 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     int lo = 0, hi = num_seqs - 1;  // last b whose segments start at or before x
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (Hkv * s_cum[mid] <= x) lo = mid; else hi = mid - 1;
+      if (mult * s_cum[mid] <= x) lo = mid; else hi = mid - 1;
     }
     c.b = lo;
     c.n = s_cum[lo + 1] - s_cum[lo];
-    const int off = x - Hkv * s_cum[lo];
-    c.g = off / c.n;
-    c.k = off - c.g * c.n;
+    const int off = x - mult * s_cum[lo];
+    c.g = HPW > 0 ? g_lane : off / c.n;
+    c.k = HPW > 0 ? off : off - c.g * c.n;
     c.seg_start = x - c.k;
   };
   auto finish_desc = [&](Chunk& c, bool starts_piece) {
@@ -149,11 +155,15 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
       bt_reg = bt_base + lane < bt_stride ? block_tables[(int64_t)c.b * bt_stride + bt_base + lane] : -1;
     }
     const int64_t head_off = (int64_t)c.g * D + sub * EPL;
+    // a chunk inside one block (the usual case for blocks of >= 32 keys) reads its block id
+    // once from the window with a scalar lane read; otherwise each row shuffles its own
+    const bool one_block = first == last;
+    const int blk0 = __builtin_amdgcn_readlane(bt_reg, min(first - bt_base, 63));
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = i * RPI + rsub;
       const int j = c.k + r;
-      const int blk = __shfl(bt_reg, min((j >> bs_log2) - bt_base, 63));
+      const int blk = one_block ? blk0 : __shfl(bt_reg, min((j >> bs_log2) - bt_base, 63));
       kr[i] = u32x4_t{0u, 0u, 0u, 0u};
       vr[i] = u32x4_t{0u, 0u, 0u, 0u};
       if (r < c.cnt) {
@@ -247,17 +257,17 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     for (int h = 0; h < G; ++h) {
       float mall = m[h];
 #pragma unroll
-      for (int msk = LPR; msk < 64; msk <<= 1) mall = fmaxf(mall, __shfl_xor(mall, msk));
+      for (int msk = RSTRIDE; msk < 64; msk <<= 1) mall = fmaxf(mall, __shfl_xor(mall, msk));
       const float muse = mall == -INFINITY ? 0.f : mall;
       const float sc = __builtin_amdgcn_exp2f(m[h] - muse);
       float lt = l[h] * sc;
 #pragma unroll
-      for (int msk = LPR; msk < 64; msk <<= 1) lt += __shfl_xor(lt, msk);
+      for (int msk = RSTRIDE; msk < 64; msk <<= 1) lt += __shfl_xor(lt, msk);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         float v = o[h][e] * sc;
 #pragma unroll
-        for (int msk = LPR; msk < 64; msk <<= 1) v += __shfl_xor(v, msk);
+        for (int msk = RSTRIDE; msk < 64; msk <<= 1) v += __shfl_xor(v, msk);
         o[h][e] = v;
       }
       m[h] = mall;
@@ -342,7 +352,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(
     T* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t cap, int32_t Hq,
     int32_t Hkv, int32_t max_pieces, const float* __restrict__ ws_o,
-    const float* __restrict__ ws_ml, const int32_t* __restrict__ ws_meta) {
+    const float* __restrict__ ws_ml, const int32_t* __restrict__ ws_meta, int32_t per_seq_line) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int n = clamp_ctx(context_lens[b], cap);
   T* dst = out + ((int64_t)b * Hq + h) * D + d;
@@ -352,7 +362,8 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(
   }
   const int S = ws_meta[0];
   const int g = h / (Hq / Hkv);
-  const int seg_start = Hkv * ws_meta[1 + b] + g * n;
+  // start of the segment on the split line: one per (sequence, kv head), or one per sequence
+  const int seg_start = per_seq_line ? ws_meta[1 + b] : Hkv * ws_meta[1 + b] + g * n;
   const int np = (seg_start + n - 1) / S - seg_start / S + 1;
   if (np == 1) return;  // written by the stream kernel
   const int64_t base = ((int64_t)b * Hq + h) * max_pieces;
@@ -367,34 +378,53 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(
   Elem<T>::store(dst, acc / L);
 }
 
-template <typename T, int D, int G, int NI>
+template <typename T, int D, int G, int NI, int HPW>
 static int run_decode(const DecodeArgs& a, hipStream_t stream) {
   const int bs_log2 = __builtin_ctz((unsigned)a.block_size);
   const float c = a.scale * kLog2e;
   const int64_t cap = (int64_t)a.max_blocks_per_seq * a.block_size;
-  const int64_t upper = (int64_t)a.num_seqs * cap * a.num_kv_heads;  // keys at full contexts
-  int64_t blocks = (upper + 4LL * a.partition - 1) / (4LL * a.partition);
+  // share owners: workgroups (HPW > 0) or wavefronts, never more than min_keys keys apart
+  const int64_t upper = (int64_t)a.num_seqs * cap * (HPW > 0 ? 1 : a.num_kv_heads);
+  const int64_t per_block = HPW > 0 ? a.partition : 4LL * a.partition;
+  int64_t blocks = (upper + per_block - 1) / per_block;
   if (blocks > a.max_workgroups) blocks = a.max_workgroups;
   if (blocks < 1) blocks = 1;
   const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
-  hipLaunchKernelGGL((decode_stream_kernel<T, D, G, NI>), dim3((unsigned)blocks), dim3(256), lds,
-                     stream, (T*)a.out, (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache,
-                     a.num_blocks, a.block_tables, a.max_blocks_per_seq, a.context_lens,
-                     a.num_seqs, a.num_kv_heads, bs_log2, c, a.partition, a.max_parts, a.ws_o,
-                     a.ws_ml, a.ws_meta);
+  hipLaunchKernelGGL((decode_stream_kernel<T, D, G, NI, HPW>), dim3((unsigned)blocks), dim3(256),
+                     lds, stream, (T*)a.out, (const T*)a.q, (const T*)a.k_cache,
+                     (const T*)a.v_cache, a.num_blocks, a.block_tables, a.max_blocks_per_seq,
+                     a.context_lens, a.num_seqs, a.num_kv_heads, bs_log2, c, a.partition,
+                     a.max_parts, a.ws_o, a.ws_ml, a.ws_meta);
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.num_heads, a.num_seqs), dim3(D), 0,
                      stream, (T*)a.out, a.context_lens, (int32_t)cap, a.num_heads,
-                     a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta);
+                     a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, HPW > 0 ? 1 : 0);
   return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// Whole token rows per workgroup when the kv heads split evenly over its 4 wavefronts and
+// one load instruction still covers whole rows; otherwise one head per wavefront share.
+template <typename T, int D, int G, int NI>
+static int run_decode_hpw(const DecodeArgs& a, hipStream_t s) {
+  constexpr int LPR = D / Elem<T>::kPerChunk;
+  switch (a.num_kv_heads % 4 == 0 ? a.num_kv_heads / 4 : 0) {
+    case 1: return run_decode<T, D, G, NI, 1>(a, s);
+    case 2:
+      if constexpr (2 * LPR <= 64) return run_decode<T, D, G, NI, 2>(a, s);
+      return run_decode<T, D, G, NI, 0>(a, s);
+    case 4:
+      if constexpr (4 * LPR <= 64) return run_decode<T, D, G, NI, 4>(a, s);
+      return run_decode<T, D, G, NI, 0>(a, s);
+    default: return run_decode<T, D, G, NI, 0>(a, s);
+  }
 }
 
 template <typename T, int D>
 static int dispatch_g(const DecodeArgs& a, hipStream_t s) {
   switch (a.num_heads / a.num_kv_heads) {
-    case 1: return run_decode<T, D, 1, 8>(a, s);
-    case 2: return run_decode<T, D, 2, 8>(a, s);
-    case 4: return run_decode<T, D, 4, 4>(a, s);
-    case 8: return run_decode<T, D, 8, 2>(a, s);
+    case 1: return run_decode_hpw<T, D, 1, 8>(a, s);
+    case 2: return run_decode_hpw<T, D, 2, 8>(a, s);
+    case 4: return run_decode_hpw<T, D, 4, 4>(a, s);
+    case 8: return run_decode_hpw<T, D, 8, 2>(a, s);
     default: return -2;
   }
 }
