@@ -136,6 +136,7 @@ int store_kvcache(const void* key, int64_t key_token_stride,
  *                partition_size), owned by the caller; no initial contents needed; in use
  *                until the stream passes the end of the call, so calls that overlap on
  *                different streams need different workspaces.
+ * out, q, k_cache, v_cache and workspace must be 16-byte aligned (PKV_ERR_INVALID otherwise).
  * Preconditions: num_blocks >= 1; n <= max_blocks_per_seq * bs (larger n is clamped to
  * that); table entries below ceil(n / bs) lie in [0, num_blocks) - an entry outside it is
  * not dereferenced and turns that sequence's output row into NaN.
@@ -172,6 +173,7 @@ int paged_attn_decode(void* out, const void* q,
  *   max_seqlen_q host int: an upper bound of every Lq (sizes the launch, as in the
  *                engine's Context); max_seqlen_k is accepted for the same interface.
  *   causal       must be 1 (the engine always attends causally).
+ * out, q, k_cache and v_cache must be 16-byte aligned (PKV_ERR_INVALID otherwise).
  * Preconditions: cu_seqlens_q[num_seqs] == total_q; Lq <= max_seqlen_q (rows past it are
  * left unwritten); Lk >= Lq; Lk <= max_blocks_per_seq * bs (larger Lk is clamped); table
  * entries below ceil(Lk / bs) lie in [0, num_blocks) - an entry outside it is not

@@ -19,6 +19,9 @@ bool supported_group(int32_t heads, int32_t kv_heads) {
 }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The attention kernels move rows in 16-byte vector accesses.
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 int decode_parts(int32_t max_blocks_per_seq, int32_t block_size, int32_t partition,
                  int32_t* part_out, int64_t* max_parts_out) {
   const int32_t part = partition == 0 ? pkv::kDecodeDefaultPartition : partition;
@@ -201,6 +204,9 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
                                                         max_blocks_per_seq, block_size,
                                                         partition_size);
   if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(workspace))
+    return PKV_ERR_INVALID;
   pkv::DecodeArgs a;
   a.out = out;
   a.q = q;
@@ -253,6 +259,8 @@ int paged_attn_prefill_varlen(void* out, const void* q, const void* k_cache, con
   if (num_seqs > 65535 || ceil_div(max_seqlen_q, 64) > 65535) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens_q || !cu_seqlens_k)
+    return PKV_ERR_INVALID;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return PKV_ERR_INVALID;
   pkv::PrefillArgs a;
   a.out = out;

@@ -347,35 +347,103 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   }
 }
 
-// Merges the partial slots of every (sequence, query head) whose segment was split.
+// Merges the partial slots of every (sequence, query head) whose segment was split: one
+// wavefront per (sequence, head), four per workgroup. The kernel is latency bound, so it
+// takes two rounds of loads: first the split metadata together with the (m, l) of the
+// first 64 slots (lane p holds slot p; the slots exist for every row, so they are read
+// before the row's slot count is known), then the o rows of up to 16 slots at a time,
+// D / 64 consecutive floats per lane (one coalesced row per load instruction).
 template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(
-    T* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t cap, int32_t Hq,
-    int32_t Hkv, int32_t max_pieces, const float* __restrict__ ws_o,
-    const float* __restrict__ ws_ml, const int32_t* __restrict__ ws_meta, int32_t per_seq_line) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int n = clamp_ctx(context_lens[b], cap);
-  T* dst = out + ((int64_t)b * Hq + h) * D + d;
-  if (n == 0) {
-    Elem<T>::store(dst, 0.f);
-    return;
-  }
+__global__ __launch_bounds__(256) void decode_combine_kernel(
+    T* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t cap,
+    int32_t num_rows, int32_t Hq, int32_t Hkv, int32_t max_pieces,
+    const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
+    const int32_t* __restrict__ ws_meta, int32_t per_seq_line) {
+  constexpr int DPL = D / 64;  // floats per lane
+  constexpr int OB = 16;       // o rows per load batch
+  static_assert(DPL == 1 || DPL == 2, "head_dim 64 or 128");
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // b * Hq + h
+  if (row >= num_rows) return;
+  const int b = row / Hq, h = row - b * Hq;
+  const int64_t base = (int64_t)row * max_pieces;
+  // round 1
+  const int n_raw = context_lens[b];
   const int S = ws_meta[0];
-  const int g = h / (Hq / Hkv);
-  // start of the segment on the split line: one per (sequence, kv head), or one per sequence
-  const int seg_start = per_seq_line ? ws_meta[1 + b] : Hkv * ws_meta[1 + b] + g * n;
-  const int np = (seg_start + n - 1) / S - seg_start / S + 1;
-  if (np == 1) return;  // written by the stream kernel
-  const int64_t base = ((int64_t)b * Hq + h) * max_pieces;
-  float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ws_ml[2 * (base + p)]);
-  float L = 0.f, acc = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const float wgt = __builtin_amdgcn_exp2f(ws_ml[2 * (base + p)] - M);
-    L = fmaf(wgt, ws_ml[2 * (base + p) + 1], L);
-    acc = fmaf(wgt, ws_o[(base + p) * D + d], acc);
+  const int cum = ws_meta[1 + b];
+  float mp = -INFINITY, lp = 0.f;
+  if (lane < max_pieces) {
+    mp = ws_ml[2 * (base + lane)];
+    lp = ws_ml[2 * (base + lane) + 1];
   }
-  Elem<T>::store(dst, acc / L);
+  const int n = clamp_ctx(n_raw, cap);
+  T* dst = out + (int64_t)row * D + lane * DPL;
+  float acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  float L = 1.f;  // a sequence with context length 0 gets a zero row
+  if (n > 0) {
+    const int g = h / (Hq / Hkv);
+    // start of the segment on the split line: one per (sequence, kv head), or one per sequence
+    const int seg_start = per_seq_line ? cum : Hkv * cum + g * n;
+    const int np = (seg_start + n - 1) / S - seg_start / S + 1;
+    if (np == 1) return;  // written by the stream kernel
+    float M = -INFINITY;
+    L = 0.f;
+    for (int p0 = 0; p0 < np; p0 += 64) {
+      const int cnt = min(64, np - p0);
+      if (p0 > 0) {  // slots past the first 64 (segments cut into more than 64 pieces)
+        mp = -INFINITY;
+        lp = 0.f;
+        if (lane < cnt) {
+          mp = ws_ml[2 * (base + p0 + lane)];
+          lp = ws_ml[2 * (base + p0 + lane) + 1];
+        }
+      } else if (lane >= cnt) {
+        mp = -INFINITY;
+        lp = 0.f;
+      }
+      const float Mn = fmaxf(M, group_max<64>(mp));
+      const float rescale = __builtin_amdgcn_exp2f(M - Mn);
+      const float wp = lane < cnt ? __builtin_amdgcn_exp2f(mp - Mn) : 0.f;
+      L = fmaf(L, rescale, group_sum<64>(wp * lp));
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] *= rescale;
+      M = Mn;
+      // round 2: the o rows
+      for (int p = 0; p < cnt; p += OB) {
+        float ov[OB][DPL];
+#pragma unroll
+        for (int u = 0; u < OB; ++u) {
+          const float* src = ws_o + (base + p0 + min(p + u, cnt - 1)) * D + lane * DPL;
+          if constexpr (DPL == 2) {
+            const float2 v = *reinterpret_cast<const float2*>(src);
+            ov[u][0] = v.x;
+            ov[u][1] = v.y;
+          } else {
+            ov[u][0] = *src;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < OB; ++u) {
+          if (p + u >= cnt) break;
+          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wp), p + u));
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, ov[u][e], acc[e]);
+        }
+      }
+    }
+  }
+  const float inv = 1.f / L;
+  if constexpr (DPL == 2) {
+    if constexpr (Elem<T>::kBytes == 2) {
+      *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    } else {
+      *reinterpret_cast<float2*>(dst) = float2{acc[0] * inv, acc[1] * inv};
+    }
+  } else {
+    Elem<T>::store(dst, acc[0] * inv);
+  }
 }
 
 template <typename T, int D, int G, int NI, int HPW>
@@ -395,8 +463,9 @@ static int run_decode(const DecodeArgs& a, hipStream_t stream) {
                      (const T*)a.v_cache, a.num_blocks, a.block_tables, a.max_blocks_per_seq,
                      a.context_lens, a.num_seqs, a.num_kv_heads, bs_log2, c, a.partition,
                      a.max_parts, a.ws_o, a.ws_ml, a.ws_meta);
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.num_heads, a.num_seqs), dim3(D), 0,
-                     stream, (T*)a.out, a.context_lens, (int32_t)cap, a.num_heads,
+  const int rows = a.num_seqs * a.num_heads;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256),
+                     0, stream, (T*)a.out, a.context_lens, (int32_t)cap, rows, a.num_heads,
                      a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, HPW > 0 ? 1 : 0);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

@@ -138,7 +138,11 @@ def _prefill_rc(**kw):
     (dict(D=96), -2), (dict(Hq=6, Hkv=2), -2), (dict(Hq=5, Hkv=2), -1), (dict(bs=24), -2),
     (dict(bs=8), -2), (dict(dt=7), -2), (dict(part=100), -1), (dict(part=2048), -1),
     (dict(ws_bytes=16), -3), (dict(ws=None), -3), (dict(q=None), -1), (dict(B=0), 0),
-    (dict(W=0), -1),
+    (dict(W=0), -1), (dict(nb=0), -1),
+    # 16-byte vector rows: misaligned out, q, caches or workspace are rejected
+    (dict(out=ctypes.c_void_p(0x1002)), -1), (dict(q=ctypes.c_void_p(0x1008)), -1),
+    (dict(k=ctypes.c_void_p(0x1004)), -1), (dict(v=ctypes.c_void_p(0x100c)), -1),
+    (dict(ws=ctypes.c_void_p(0x1008)), -1),
 ])
 def test_decode_argument_validation(kw, status):
     assert _decode_rc(**kw) == status
@@ -147,6 +151,8 @@ def test_decode_argument_validation(kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(dt=B.PKV_F32), -2), (dict(causal=0), -2), (dict(D=80), -2), (dict(Hq=12, Hkv=4), -2),
     (dict(bs=100), -2), (dict(q=None), -1), (dict(B=0), 0), (dict(T=0), 0), (dict(mq=0), 0),
+    (dict(out=ctypes.c_void_p(0x1002)), -1), (dict(q=ctypes.c_void_p(0x1008)), -1),
+    (dict(k=ctypes.c_void_p(0x1004)), -1), (dict(v=ctypes.c_void_p(0x100c)), -1),
 ])
 def test_prefill_argument_validation(kw, status):
     assert _prefill_rc(**kw) == status
