@@ -28,6 +28,7 @@
 // never read from the cache, so padding entries and unused NaN slots cannot reach an MFMA.
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -36,6 +37,17 @@
 namespace pkv {
 
 constexpr int kBK = 64;  // keys per tile
+constexpr int kQueueSlots = 64;
+constexpr float kSlack = 8.f;  // log2 units a tile max may exceed the reference max  // prefill calls that may be in flight on one device at once
+
+// Work queues of the persistent prefill grid, one per call in flight (slot = call number
+// modulo kQueueSlots): [0] the next unit to hand out, [1] workgroups finished. Zero when the
+// module loads; the last workgroup of a call zeroes its slot again.
+__device__ unsigned g_prefill_queue[kQueueSlots][2];
+
+__device__ __forceinline__ unsigned atomic_add_u32(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 constexpr int kBQ = 64;  // query positions per workgroup
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -73,13 +85,15 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
 #endif
 }
 
-template <int D, int GH>
+// BIG_BLOCKS: blocks hold >= 64 keys, so every 64-key tile lies inside one block.
+template <int D, int GH, bool BIG_BLOCKS>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(
     __bf16* __restrict__ out, const __bf16* __restrict__ q, const __bf16* __restrict__ k_cache,
     const __bf16* __restrict__ v_cache, int32_t num_blocks,
     const int32_t* __restrict__ block_tables, int32_t bt_stride,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_heads,
-    int32_t num_kv_heads, int32_t bs_log2, float scale_log2e) {
+    int32_t num_kv_heads, int32_t bs_log2, float scale_log2e, int32_t num_seqs,
+    int32_t n_units, int32_t slot) {
   constexpr int KS = D / 32;                 // k-steps of the QK^T product
   constexpr int DT = D / 16;                 // 16-row tiles of O^T
   constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
@@ -93,280 +107,383 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   __shared__ __attribute__((aligned(1024))) char lds_a[2][TILEB];  // [K=0,V=1]
   __shared__ __attribute__((aligned(1024))) char lds_b[2][TILEB];
 
-  const int hg = blockIdx.x, b = blockIdx.y, t = blockIdx.z;
-  const int G = num_heads / num_kv_heads;
-  const int h0 = hg * GH, g = h0 / G;
-  const int q_begin = cu_q[b];
-  const int Lq = cu_q[b + 1] - q_begin;
-  const int cap = bt_stride << bs_log2;
-  int Lk = cu_k[b + 1] - cu_k[b];
-  Lk = Lk > cap ? cap : Lk;
-  const int i_hi = Lq - kBQ * t;  // exclusive end of this unit's query rows
-  if (i_hi <= 0) return;
-  const int i_lo = i_hi - kBQ;    // may be negative: those rows are idle
-  const int off = Lk - Lq;        // position of query row 0
+  // ---- persistent workgroups over a queue of units. Unit u = (query tile t counted from the
+  // sequence end, sequence b, head group hg), t-major: the longest rows (most keys) of every
+  // sequence come first. A workgroup claims its next unit while working on the current one.
+  __shared__ int s_next;
+  unsigned* const queue = g_prefill_queue[slot];  // [0]: next unit, [1]: workgroups done
+  const int n_hg = num_heads / GH;
+  auto unit = [&](const int hg, const int b, const int t) {
+    const int G = num_heads / num_kv_heads;
+    const int h0 = hg * GH, g = h0 / G;
+    const int q_begin = cu_q[b];
+    const int Lq = cu_q[b + 1] - q_begin;
+    const int cap = bt_stride << bs_log2;
+    int Lk = cu_k[b + 1] - cu_k[b];
+    Lk = Lk > cap ? cap : Lk;
+    const int i_hi = Lq - kBQ * t;  // exclusive end of this unit's query rows
+    if (i_hi <= 0) return;
+    const int i_lo = i_hi - kBQ;    // may be negative: those rows are idle
+    const int off = Lk - Lq;        // position of query row 0
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int col = lane & 15, quad = lane >> 4;
-  const int i_row = i_lo + wave * 16 + col;
-  const bool row_ok = i_row >= 0;
-  const int pos = off + i_row;
-  const int kend = min(Lk, off + i_hi);
-  const int n_kt = kend > 0 ? (kend + kBK - 1) / kBK : 0;
-  const int wave_min_pos = off + i_lo + wave * 16;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, quad = lane >> 4;
+    const int i_row = i_lo + wave * 16 + col;
+    const bool row_ok = i_row >= 0;
+    const int pos = off + i_row;
+    const int kend = min(Lk, off + i_hi);
+    const int n_kt = kend > 0 ? (kend + kBK - 1) / kBK : 0;
+    const int wave_min_pos = off + i_lo + wave * 16;
 
-  const int64_t row_elems = (int64_t)num_kv_heads * D;
-  const int32_t* bt = block_tables + (int64_t)b * bt_stride;
-  const int bs_mask = (1 << bs_log2) - 1;
+    const int64_t row_elems = (int64_t)num_kv_heads * D;
+    const int32_t* bt = block_tables + (int64_t)b * bt_stride;
+    const int bs_mask = (1 << bs_log2) - 1;
 
-  // Q^T operands: lane holds 8 dims of its query column for each k-step
-  bf16x8_t qb[GH][KS];
-#pragma unroll
-  for (int nt = 0; nt < GH; ++nt)
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (row_ok)
-        v = load16(q + ((int64_t)(q_begin + i_row) * num_heads + h0 + nt) * D + 32 * s + 8 * quad);
-      qb[nt][s] = __builtin_bit_cast(bf16x8_t, v);
-    }
+    // Q^T operands: lane holds 8 dims of its query column for each k-step
+    bf16x8_t qb[GH][KS];
+  #pragma unroll
+    for (int nt = 0; nt < GH; ++nt)
+  #pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+        if (row_ok)
+          v = load16(q + ((int64_t)(q_begin + i_row) * num_heads + h0 + nt) * D + 32 * s + 8 * quad);
+        qb[nt][s] = __builtin_bit_cast(bf16x8_t, v);
+      }
 
-  // ---- direct HBM -> LDS tile loads -------------------------------------------------------
-  // Instruction i of this wave fills LDS bytes [(wave*NL + i) * 1024, +1024) of a tile: rows
-  // RPL * (wave*NL + i) + lane / CPR, slot lane % CPR. K slot s of row r holds chunk
-  // s ^ (r % CPR); V slot s holds chunk 2 * ((s/2) ^ (r % (CPR/2))) + s % 2 (32-byte swizzle).
-  int lrow[NL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i) lrow[i] = RPL * (wave * NL + i) + lane / CPR;
-  const int slot = lane % CPR;
-  int kchunk[NL], vchunk[NL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    kchunk[i] = slot ^ (lrow[i] % CPR);
-    vchunk[i] = 2 * ((slot >> 1) ^ (lrow[i] % (CPR / 2))) + (slot & 1);
-  }
-  int nblk[NL];  // block ids of this lane's rows for a tile two steps ahead
-  auto fetch_blocks = [&](int kt) {
-#pragma unroll
+    // ---- direct HBM -> LDS tile loads -------------------------------------------------------
+    // Instruction i of this wave fills LDS bytes [(wave*NL + i) * 1024, +1024) of a tile: rows
+    // RPL * (wave*NL + i) + lane / CPR, slot lane % CPR. K slot s of row r holds chunk
+    // s ^ (r % CPR); V slot s holds chunk 2 * ((s/2) ^ (r % (CPR/2))) + s % 2 (32-byte swizzle).
+    int lrow[NL];
+  #pragma unroll
+    for (int i = 0; i < NL; ++i) lrow[i] = RPL * (wave * NL + i) + lane / CPR;
+    const int slot = lane % CPR;
+    int kchunk[NL], vchunk[NL];
+  #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int j = kt * kBK + lrow[i];
-      nblk[i] = (kt < n_kt && j < Lk) ? bt[j >> bs_log2] : -1;
+      kchunk[i] = slot ^ (lrow[i] % CPR);
+      vchunk[i] = 2 * ((slot >> 1) ^ (lrow[i] % (CPR / 2))) + (slot & 1);
     }
-  };
-  auto issue_tile = [&](int kt, char (*dst)[TILEB], const int* blk) {
-    bool ok[NL];
-    bool all_ok = true;
-#pragma unroll
+    // BIG_BLOCKS: a tile's rows need one block id, and their addresses are that block's
+    // base plus a per-lane constant. Otherwise every row looks its block up.
+    int lane_off_k[NL], lane_off_v[NL];  // elements from the tile's first row
+  #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int j = kt * kBK + lrow[i];
-      ok[i] = j < Lk && (unsigned)blk[i] < (unsigned)num_blocks;
-      all_ok &= ok[i];
+      lane_off_k[i] = lrow[i] * (int)row_elems + g * D + 8 * kchunk[i];
+      lane_off_v[i] = lrow[i] * (int)row_elems + g * D + 8 * vchunk[i];
     }
-    if (__all(all_ok)) {  // every row of the tile is a real key: loads only, no branches
-#pragma unroll
+    int nblk[NL];  // block ids of this lane's rows for a tile two steps ahead
+    auto fetch_blocks = [&](int kt) {
+      if constexpr (BIG_BLOCKS) {  // one id, the same for every lane (nblk[1..] unused)
+        nblk[0] = kt < n_kt ? bt[(kt * kBK) >> bs_log2] : -1;
+        return;
+      }
+  #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const int j = kt * kBK + lrow[i];
-        const int64_t rowoff =
-            (int64_t)((blk[i] << bs_log2) + (j & bs_mask)) * row_elems + (int64_t)g * D;
-        load_lds16(k_cache + rowoff + 8 * kchunk[i], &dst[0][(wave * NL + i) * 1024]);
-        load_lds16(v_cache + rowoff + 8 * vchunk[i], &dst[1][(wave * NL + i) * 1024]);
+        nblk[i] = (kt < n_kt && j < Lk) ? bt[j >> bs_log2] : -1;
       }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int j = kt * kBK + lrow[i];
-      char* kdst = &dst[0][(wave * NL + i) * 1024];
-      char* vdst = &dst[1][(wave * NL + i) * 1024];
-      if (ok[i]) {
-        const int64_t rowoff =
-            (int64_t)((blk[i] << bs_log2) + (j & bs_mask)) * row_elems + (int64_t)g * D;
-        load_lds16(k_cache + rowoff + 8 * kchunk[i], kdst);
-        load_lds16(v_cache + rowoff + 8 * vchunk[i], vdst);
-      } else {
-        // past the sequence: zeros; a bad block id: NaN (poisons only this sequence's rows)
-        const u32x4_t fill = j < Lk ? Elem<__bf16>::nan_chunk() : u32x4_t{0u, 0u, 0u, 0u};
-        store16(kdst + 16 * lane, fill);
-        store16(vdst + 16 * lane, fill);
-      }
-    }
-  };
-
-  f32x4_t oacc[DT][GH];
-#pragma unroll
-  for (int i = 0; i < DT; ++i)
-#pragma unroll
-    for (int nt = 0; nt < GH; ++nt) oacc[i][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[GH], l_run[GH];
-#pragma unroll
-  for (int nt = 0; nt < GH; ++nt) {
-    m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
-  }
-
-  int cblk[NL];
-  if (n_kt > 0) {
-    fetch_blocks(0);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) cblk[i] = nblk[i];
-    wait_vmem();
-    issue_tile(0, lds_a, cblk);
-    fetch_blocks(1);
-  }
-  auto tile_step = [&](int kt, char (*cur)[TILEB], char (*nxt)[TILEB]) {
-    wait_vmem();          // this wave's part of tile kt (and the block ids of tile kt+1)
-    __syncthreads();      // every wave's part; every wave is done with the other buffer
-    if (kt + 1 < n_kt) {
-#pragma unroll
-      for (int i = 0; i < NL; ++i) cblk[i] = nblk[i];
-      issue_tile(kt + 1, nxt, cblk);
-      fetch_blocks(kt + 2);
-    }
-    const char* Kt = cur[0];
-    const char* Vt = cur[1];
-
-    // S^T = K Q^T : sacc[mt][nt][r] = score of key kt*64 + 16 mt + 4 quad + r, column col
-    f32x4_t sacc[4][GH];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < GH; ++nt) sacc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int r = 16 * mt + col;
-        const int c = (4 * s + quad) ^ (r % CPR);
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kt + r * ROWB + 16 * c);
-#pragma unroll
-        for (int nt = 0; nt < GH; ++nt) sacc[mt][nt] = mfma16(a, qb[nt][s], sacc[mt][nt]);
-      }
-
-    // online softmax of the tile; the causal mask only on tiles that cross this wave's diagonal
-    bf16x8_t pb[2][GH];
-    bool moved = false;
-    float alpha[GH];
-    auto softmax = [&](auto masked) {
-      constexpr bool kMask = decltype(masked)::value;
-#pragma unroll
-      for (int nt = 0; nt < GH; ++nt) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if constexpr (kMask) {
-              const int j = kt * kBK + 16 * mt + 4 * quad + r;
-              if (j > pos) sacc[mt][nt][r] = -INFINITY;
-            }
-            mx = fmaxf(mx, sacc[mt][nt][r]);
+    };
+    auto issue_tile = [&](int kt, char (*dst)[TILEB], const int* blk) {
+      if constexpr (BIG_BLOCKS) {
+        const int b0 = __builtin_amdgcn_readfirstlane(blk[0]);
+        const bool blk_ok = (unsigned)b0 < (unsigned)num_blocks;
+        const int64_t base =
+            blk_ok ? ((int64_t)b0 << bs_log2 | ((kt * kBK) & bs_mask)) * row_elems : 0;
+        const __bf16* kb = k_cache + base;
+        const __bf16* vb = v_cache + base;
+        if (blk_ok && (kt + 1) * kBK <= Lk) {  // a full tile of real keys: loads only
+  #pragma unroll
+          for (int i = 0; i < NL; ++i) {
+            load_lds16(kb + lane_off_k[i], &dst[0][(wave * NL + i) * 1024]);
+            load_lds16(vb + lane_off_v[i], &dst[1][(wave * NL + i) * 1024]);
           }
-        mx = rows_max(mx);
-        const float m_new = fmaxf(m_run[nt], mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        alpha[nt] = __builtin_amdgcn_exp2f((m_run[nt] - m_use) * scale_log2e);
-        moved |= m_new != m_run[nt];
-        const float mc = m_use * scale_log2e;
-        float psum = 0.f;
-        float pv[4][4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mt][nt][r], scale_log2e, -mc));
-            pv[mt][r] = e;
-            psum += e;
+          return;
+        }
+  #pragma unroll
+        for (int i = 0; i < NL; ++i) {  // the last tile of the keys, or a bad block id
+          const int j = kt * kBK + lrow[i];
+          char* kdst = &dst[0][(wave * NL + i) * 1024];
+          char* vdst = &dst[1][(wave * NL + i) * 1024];
+          if (blk_ok && j < Lk) {
+            load_lds16(kb + lane_off_k[i], kdst);
+            load_lds16(vb + lane_off_v[i], vdst);
+          } else {
+            // past the sequence: zeros; a bad block id: NaN (poisons only this sequence's rows)
+            const u32x4_t fill = j < Lk ? Elem<__bf16>::nan_chunk() : u32x4_t{0u, 0u, 0u, 0u};
+            store16(kdst + 16 * lane, fill);
+            store16(vdst + 16 * lane, fill);
           }
-        l_run[nt] = fmaf(alpha[nt], l_run[nt], psum);
-        m_run[nt] = m_new;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          u32x4_t w;
-          w.x = pack_bf16x2(pv[2 * ks][0], pv[2 * ks][1]);
-          w.y = pack_bf16x2(pv[2 * ks][2], pv[2 * ks][3]);
-          w.z = pack_bf16x2(pv[2 * ks + 1][0], pv[2 * ks + 1][1]);
-          w.w = pack_bf16x2(pv[2 * ks + 1][2], pv[2 * ks + 1][3]);
-          pb[ks][nt] = __builtin_bit_cast(bf16x8_t, w);
+        }
+        return;
+      }
+      bool ok[NL];
+      bool all_ok = true;
+  #pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int j = kt * kBK + lrow[i];
+        ok[i] = j < Lk && (unsigned)blk[i] < (unsigned)num_blocks;
+        all_ok &= ok[i];
+      }
+      if (__all(all_ok)) {  // every row of the tile is a real key: loads only, no branches
+  #pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          const int j = kt * kBK + lrow[i];
+          const int64_t rowoff =
+              (int64_t)((blk[i] << bs_log2) + (j & bs_mask)) * row_elems + (int64_t)g * D;
+          load_lds16(k_cache + rowoff + 8 * kchunk[i], &dst[0][(wave * NL + i) * 1024]);
+          load_lds16(v_cache + rowoff + 8 * vchunk[i], &dst[1][(wave * NL + i) * 1024]);
+        }
+        return;
+      }
+  #pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int j = kt * kBK + lrow[i];
+        char* kdst = &dst[0][(wave * NL + i) * 1024];
+        char* vdst = &dst[1][(wave * NL + i) * 1024];
+        if (ok[i]) {
+          const int64_t rowoff =
+              (int64_t)((blk[i] << bs_log2) + (j & bs_mask)) * row_elems + (int64_t)g * D;
+          load_lds16(k_cache + rowoff + 8 * kchunk[i], kdst);
+          load_lds16(v_cache + rowoff + 8 * vchunk[i], vdst);
+        } else {
+          // past the sequence: zeros; a bad block id: NaN (poisons only this sequence's rows)
+          const u32x4_t fill = j < Lk ? Elem<__bf16>::nan_chunk() : u32x4_t{0u, 0u, 0u, 0u};
+          store16(kdst + 16 * lane, fill);
+          store16(vdst + 16 * lane, fill);
         }
       }
     };
-    if (kt * kBK + kBK - 1 > wave_min_pos)
-      softmax(std::true_type{});
-    else
-      softmax(std::false_type{});
-    if (__any(moved)) {
-#pragma unroll
-      for (int i = 0; i < DT; ++i)
-#pragma unroll
-        for (int nt = 0; nt < GH; ++nt) oacc[i][nt] *= alpha[nt];
+
+    f32x4_t oacc[DT][GH];
+  #pragma unroll
+    for (int i = 0; i < DT; ++i)
+  #pragma unroll
+      for (int nt = 0; nt < GH; ++nt) oacc[i][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run[GH], l_run[GH];
+  #pragma unroll
+    for (int nt = 0; nt < GH; ++nt) {
+      m_run[nt] = -INFINITY;
+      l_run[nt] = 0.f;
     }
 
-    // O^T += V^T P^T ; lane (row d = 16 i + col, group quad) reads keys 32 ks + 4 quad + 0..3
-    // and 32 ks + 16 + 4 quad + 0..3 with two transposing reads. Source lane L of a group
-    // points at key k0 + L / 4, dims 16 i + 4 (L % 4) .. + 3.
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < DT; ++i) {
-        s16x4_t part[2];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int r = 32 * ks + 16 * hf + 4 * quad + (col >> 2);
-          const int c2 = i ^ (r % (CPR / 2));  // 32-byte chunk i, swizzled
-          const char* src = Vt + r * ROWB + 32 * c2 + 8 * (col & 3);
-          part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)src);
+    int cblk[NL];
+    if (n_kt > 0) {
+      fetch_blocks(0);
+  #pragma unroll
+      for (int i = 0; i < NL; ++i) cblk[i] = nblk[i];
+      wait_vmem();
+      issue_tile(0, lds_a, cblk);
+      fetch_blocks(1);
+    }
+    auto tile_step = [&](int kt, char (*cur)[TILEB], char (*nxt)[TILEB]) {
+      wait_vmem();          // this wave's part of tile kt (and the block ids of tile kt+1)
+      __syncthreads();      // every wave's part; every wave is done with the other buffer
+      if (kt + 1 < n_kt) {
+  #pragma unroll
+        for (int i = 0; i < NL; ++i) cblk[i] = nblk[i];
+        issue_tile(kt + 1, nxt, cblk);
+        fetch_blocks(kt + 2);
+      }
+      const char* Kt = cur[0];
+      const char* Vt = cur[1];
+
+      // S^T = K Q^T : sacc[mt][nt][r] = score of key kt*64 + 16 mt + 4 quad + r, column col
+      f32x4_t sacc[4][GH];
+  #pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+  #pragma unroll
+        for (int nt = 0; nt < GH; ++nt) sacc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int s = 0; s < KS; ++s)
+  #pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int r = 16 * mt + col;
+          const int c = (4 * s + quad) ^ (r % CPR);
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kt + r * ROWB + 16 * c);
+  #pragma unroll
+          for (int nt = 0; nt < GH; ++nt) sacc[mt][nt] = mfma16(a, qb[nt][s], sacc[mt][nt]);
         }
-        u32x4_t w;
-        w.x = __builtin_bit_cast(u32x2_t, part[0]).x;
-        w.y = __builtin_bit_cast(u32x2_t, part[0]).y;
-        w.z = __builtin_bit_cast(u32x2_t, part[1]).x;
-        w.w = __builtin_bit_cast(u32x2_t, part[1]).y;
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, w);
-#pragma unroll
-        for (int nt = 0; nt < GH; ++nt) oacc[i][nt] = mfma16(av, pb[ks][nt], oacc[i][nt]);
-      }
-  };
-  for (int kt = 0; kt < n_kt; kt += 2) {
-    tile_step(kt, lds_a, lds_b);
-    if (kt + 1 < n_kt) tile_step(kt + 1, lds_b, lds_a);
-  }
 
-  // normalise and store: lane holds dims 16 i + 4 quad + r of its query column
-#pragma unroll
-  for (int nt = 0; nt < GH; ++nt) {
-    const float inv = 1.f / rows_sum(l_run[nt]);
-    if (row_ok) {
-      __bf16* orow = out + ((int64_t)(q_begin + i_row) * num_heads + h0 + nt) * D;
-#pragma unroll
-      for (int i = 0; i < DT; ++i) {
-        u32x2_t w;
-        w.x = pack_bf16x2(oacc[i][nt][0] * inv, oacc[i][nt][1] * inv);
-        w.y = pack_bf16x2(oacc[i][nt][2] * inv, oacc[i][nt][3] * inv);
-        *reinterpret_cast<u32x2_t*>(orow + 16 * i + 4 * quad) = w;
+      // online softmax of the tile; the causal mask only on tiles that cross this wave's
+      // diagonal. The reference max of a column (m_run) moves only when a tile's max exceeds
+      // it by more than kSlack in log2 units (or was -inf): probabilities stay <= 2^kSlack,
+      // O and l share the reference, and most tiles skip rescaling O altogether.
+      bf16x8_t pb[2][GH];
+      float mxs[GH];
+      auto softmax = [&](auto masked) {
+        constexpr bool kMask = decltype(masked)::value;
+        bool need = false;
+  #pragma unroll
+        for (int nt = 0; nt < GH; ++nt) {
+          float mx = -INFINITY;
+  #pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if constexpr (kMask) {
+                const int j = kt * kBK + 16 * mt + 4 * quad + r;
+                if (j > pos) sacc[mt][nt][r] = -INFINITY;
+              }
+              mx = fmaxf(mx, sacc[mt][nt][r]);
+            }
+          mxs[nt] = rows_max(mx);
+          need |= (mxs[nt] - m_run[nt]) * scale_log2e > kSlack || (m_run[nt] == -INFINITY && mxs[nt] != -INFINITY);
+        }
+        if (__any(need)) {
+  #pragma unroll
+          for (int nt = 0; nt < GH; ++nt) {
+            const float m_new = fmaxf(m_run[nt], mxs[nt]);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f((m_run[nt] - m_use) * scale_log2e);
+            l_run[nt] *= alpha;
+  #pragma unroll
+            for (int i = 0; i < DT; ++i) oacc[i][nt] *= alpha;
+            m_run[nt] = m_new;
+          }
+        }
+  #pragma unroll
+        for (int nt = 0; nt < GH; ++nt) {
+          const float mc = (m_run[nt] == -INFINITY ? 0.f : m_run[nt]) * scale_log2e;
+          float psum = 0.f;
+          float pv[4][4];
+  #pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mt][nt][r], scale_log2e, -mc));
+              pv[mt][r] = e;
+              psum += e;
+            }
+          l_run[nt] += psum;
+  #pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            u32x4_t w;
+            w.x = pack_bf16x2(pv[2 * ks][0], pv[2 * ks][1]);
+            w.y = pack_bf16x2(pv[2 * ks][2], pv[2 * ks][3]);
+            w.z = pack_bf16x2(pv[2 * ks + 1][0], pv[2 * ks + 1][1]);
+            w.w = pack_bf16x2(pv[2 * ks + 1][2], pv[2 * ks + 1][3]);
+            pb[ks][nt] = __builtin_bit_cast(bf16x8_t, w);
+          }
+        }
+      };
+      if (kt * kBK + kBK - 1 > wave_min_pos)
+        softmax(std::true_type{});
+      else
+        softmax(std::false_type{});
+
+      // O^T += V^T P^T ; lane (row d = 16 i + col, group quad) reads keys 32 ks + 4 quad + 0..3
+      // and 32 ks + 16 + 4 quad + 0..3 with two transposing reads. Source lane L of a group
+      // points at key k0 + L / 4, dims 16 i + 4 (L % 4) .. + 3.
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+  #pragma unroll
+        for (int i = 0; i < DT; ++i) {
+          s16x4_t part[2];
+  #pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int r = 32 * ks + 16 * hf + 4 * quad + (col >> 2);
+            const int c2 = i ^ (r % (CPR / 2));  // 32-byte chunk i, swizzled
+            const char* src = Vt + r * ROWB + 32 * c2 + 8 * (col & 3);
+            part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)src);
+          }
+          u32x4_t w;
+          w.x = __builtin_bit_cast(u32x2_t, part[0]).x;
+          w.y = __builtin_bit_cast(u32x2_t, part[0]).y;
+          w.z = __builtin_bit_cast(u32x2_t, part[1]).x;
+          w.w = __builtin_bit_cast(u32x2_t, part[1]).y;
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, w);
+  #pragma unroll
+          for (int nt = 0; nt < GH; ++nt) oacc[i][nt] = mfma16(av, pb[ks][nt], oacc[i][nt]);
+        }
+    };
+    for (int kt = 0; kt < n_kt; kt += 2) {
+      tile_step(kt, lds_a, lds_b);
+      if (kt + 1 < n_kt) tile_step(kt + 1, lds_b, lds_a);
+    }
+
+    // normalise and store: lane holds dims 16 i + 4 quad + r of its query column
+  #pragma unroll
+    for (int nt = 0; nt < GH; ++nt) {
+      const float inv = 1.f / rows_sum(l_run[nt]);
+      if (row_ok) {
+        __bf16* orow = out + ((int64_t)(q_begin + i_row) * num_heads + h0 + nt) * D;
+  #pragma unroll
+        for (int i = 0; i < DT; ++i) {
+          u32x2_t w;
+          w.x = pack_bf16x2(oacc[i][nt][0] * inv, oacc[i][nt][1] * inv);
+          w.y = pack_bf16x2(oacc[i][nt][2] * inv, oacc[i][nt][3] * inv);
+          *reinterpret_cast<u32x2_t*>(orow + 16 * i + 4 * quad) = w;
+        }
       }
     }
+  };
+  if (threadIdx.x == 0) s_next = (int)atomic_add_u32(queue, 1u);
+  __syncthreads();
+  int u = s_next;
+  __syncthreads();  // every thread has read s_next before it is written again
+  while (u < n_units) {
+    int claim = 0;
+    if (threadIdx.x == 0) claim = (int)atomic_add_u32(queue, 1u);
+    const int t = u / (num_seqs * n_hg);
+    const int rem = u - t * num_seqs * n_hg;
+    const int b = rem / n_hg;
+    unit(rem - b * n_hg, b, t);
+    if (threadIdx.x == 0) s_next = claim;
+    __syncthreads();  // the claim is visible, and every wave is done with this unit's tiles
+    u = s_next;
+    __syncthreads();
+  }
+  // the last workgroup out leaves the queue slot zeroed for a later call
+  if (threadIdx.x == 0 && atomic_add_u32(queue + 1, 1u) == gridDim.x - 1) {
+    __hip_atomic_store(queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(queue + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-template <int D, int GH>
+// Workgroups of `kernel` (256 threads, static LDS only) the current device holds at once.
+static int resident_workgroups(const void* kernel) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess)
+    return 0;
+  return cus * per_cu;
+}
+
+template <int D, int GH, bool BIG_BLOCKS>
 static int run_prefill(const PrefillArgs& a, hipStream_t stream) {
+  static std::atomic<unsigned> calls{0};
+  static int resident = 0;  // per kernel: the device's occupancy for it (same on every MI355X)
+  if (resident <= 0) resident = resident_workgroups((const void*)prefill_kernel<D, GH, BIG_BLOCKS>);
   const int bs_log2 = __builtin_ctz((unsigned)a.block_size);
-  const int n_tiles = (a.max_seqlen_q + kBQ - 1) / kBQ;
-  dim3 grid(a.num_heads / GH, a.num_seqs, n_tiles);
-  hipLaunchKernelGGL((prefill_kernel<D, GH>), grid, dim3(256), 0, stream, (__bf16*)a.out,
-                     (const __bf16*)a.q, (const __bf16*)a.k_cache, (const __bf16*)a.v_cache,
-                     a.num_blocks, a.block_tables, a.max_blocks_per_seq, a.cu_seqlens_q,
-                     a.cu_seqlens_k, a.num_heads, a.num_kv_heads, bs_log2,
-                     a.scale * kLog2e);
+  const int64_t n_tiles = (a.max_seqlen_q + kBQ - 1) / kBQ;
+  const int64_t n_units = n_tiles * a.num_seqs * (a.num_heads / GH);
+  if (n_units > INT32_MAX) return -2;
+  int64_t grid = resident > 0 ? resident : 512;
+  if (grid > n_units) grid = n_units;
+  const int slot = (int)(calls.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);
+  hipLaunchKernelGGL((prefill_kernel<D, GH, BIG_BLOCKS>), dim3((unsigned)grid), dim3(256), 0, stream,
+                     (__bf16*)a.out, (const __bf16*)a.q, (const __bf16*)a.k_cache,
+                     (const __bf16*)a.v_cache, a.num_blocks, a.block_tables,
+                     a.max_blocks_per_seq, a.cu_seqlens_q, a.cu_seqlens_k, a.num_heads,
+                     a.num_kv_heads, bs_log2, a.scale * kLog2e, a.num_seqs, (int32_t)n_units,
+                     slot);
   return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+template <int D, int GH>
+static int run_prefill_bs(const PrefillArgs& a, hipStream_t stream) {
+  return a.block_size >= kBK ? run_prefill<D, GH, true>(a, stream) : run_prefill<D, GH, false>(a, stream);
 }
 
 int launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0 || a.max_seqlen_q == 0) return 0;
   const int G = a.num_heads / a.num_kv_heads;
   const bool pair = (G % 2) == 0;
-  if (a.head_dim == 128) return pair ? run_prefill<128, 2>(a, stream) : run_prefill<128, 1>(a, stream);
-  if (a.head_dim == 64) return pair ? run_prefill<64, 2>(a, stream) : run_prefill<64, 1>(a, stream);
+  if (a.head_dim == 128) return pair ? run_prefill_bs<128, 2>(a, stream) : run_prefill_bs<128, 1>(a, stream);
+  if (a.head_dim == 64) return pair ? run_prefill_bs<64, 2>(a, stream) : run_prefill_bs<64, 1>(a, stream);
   return -2;
 }
 
