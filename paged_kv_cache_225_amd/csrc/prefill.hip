@@ -28,7 +28,6 @@
 // never read from the cache, so padding entries and unused NaN slots cannot reach an MFMA.
 #include <math.h>
 
-#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -37,17 +36,7 @@
 namespace pkv {
 
 constexpr int kBK = 64;  // keys per tile
-constexpr int kQueueSlots = 64;
-constexpr float kSlack = 8.f;  // log2 units a tile max may exceed the reference max  // prefill calls that may be in flight on one device at once
-
-// Work queues of the persistent prefill grid, one per call in flight (slot = call number
-// modulo kQueueSlots): [0] the next unit to hand out, [1] workgroups finished. Zero when the
-// module loads; the last workgroup of a call zeroes its slot again.
-__device__ unsigned g_prefill_queue[kQueueSlots][2];
-
-__device__ __forceinline__ unsigned atomic_add_u32(unsigned* p, unsigned v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+constexpr float kSlack = 8.f;  // log2 units a tile max may exceed the reference max
 constexpr int kBQ = 64;  // query positions per workgroup
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -92,8 +81,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     const __bf16* __restrict__ v_cache, int32_t num_blocks,
     const int32_t* __restrict__ block_tables, int32_t bt_stride,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_heads,
-    int32_t num_kv_heads, int32_t bs_log2, float scale_log2e, int32_t num_seqs,
-    int32_t n_units, int32_t slot) {
+    int32_t num_kv_heads, int32_t bs_log2, float scale_log2e) {
   constexpr int KS = D / 32;                 // k-steps of the QK^T product
   constexpr int DT = D / 16;                 // 16-row tiles of O^T
   constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
@@ -107,12 +95,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   __shared__ __attribute__((aligned(1024))) char lds_a[2][TILEB];  // [K=0,V=1]
   __shared__ __attribute__((aligned(1024))) char lds_b[2][TILEB];
 
-  // ---- persistent workgroups over a queue of units. Unit u = (query tile t counted from the
-  // sequence end, sequence b, head group hg), t-major: the longest rows (most keys) of every
-  // sequence come first. A workgroup claims its next unit while working on the current one.
-  __shared__ int s_next;
-  unsigned* const queue = g_prefill_queue[slot];  // [0]: next unit, [1]: workgroups done
-  const int n_hg = num_heads / GH;
+  // Work unit: (head group hg, sequence b, query tile t counted from the sequence end) =
+  // (blockIdx.x, blockIdx.y, blockIdx.z). x = hg runs fastest, so the workgroups of a head
+  // group - dealt round-robin to the XCDs - stay on one XCD, where all its query tiles share
+  // the K/V in L2; z = t puts the longest rows (most keys) first.
   auto unit = [&](const int hg, const int b, const int t) {
     const int G = num_heads / num_kv_heads;
     const int h0 = hg * GH, g = h0 / G;
@@ -419,57 +405,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       }
     }
   };
-  if (threadIdx.x == 0) s_next = (int)atomic_add_u32(queue, 1u);
-  __syncthreads();
-  int u = s_next;
-  __syncthreads();  // every thread has read s_next before it is written again
-  while (u < n_units) {
-    int claim = 0;
-    if (threadIdx.x == 0) claim = (int)atomic_add_u32(queue, 1u);
-    const int t = u / (num_seqs * n_hg);
-    const int rem = u - t * num_seqs * n_hg;
-    const int b = rem / n_hg;
-    unit(rem - b * n_hg, b, t);
-    if (threadIdx.x == 0) s_next = claim;
-    __syncthreads();  // the claim is visible, and every wave is done with this unit's tiles
-    u = s_next;
-    __syncthreads();
-  }
-  // the last workgroup out leaves the queue slot zeroed for a later call
-  if (threadIdx.x == 0 && atomic_add_u32(queue + 1, 1u) == gridDim.x - 1) {
-    __hip_atomic_store(queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(queue + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// Workgroups of `kernel` (256 threads, static LDS only) the current device holds at once.
-static int resident_workgroups(const void* kernel) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess)
-    return 0;
-  return cus * per_cu;
+  unit(blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 template <int D, int GH, bool BIG_BLOCKS>
 static int run_prefill(const PrefillArgs& a, hipStream_t stream) {
-  static std::atomic<unsigned> calls{0};
-  static int resident = 0;  // per kernel: the device's occupancy for it (same on every MI355X)
-  if (resident <= 0) resident = resident_workgroups((const void*)prefill_kernel<D, GH, BIG_BLOCKS>);
   const int bs_log2 = __builtin_ctz((unsigned)a.block_size);
-  const int64_t n_tiles = (a.max_seqlen_q + kBQ - 1) / kBQ;
-  const int64_t n_units = n_tiles * a.num_seqs * (a.num_heads / GH);
-  if (n_units > INT32_MAX) return -2;
-  int64_t grid = resident > 0 ? resident : 512;
-  if (grid > n_units) grid = n_units;
-  const int slot = (int)(calls.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);
-  hipLaunchKernelGGL((prefill_kernel<D, GH, BIG_BLOCKS>), dim3((unsigned)grid), dim3(256), 0, stream,
+  const int n_tiles = (a.max_seqlen_q + kBQ - 1) / kBQ;
+  dim3 grid(a.num_heads / GH, a.num_seqs, n_tiles);
+  hipLaunchKernelGGL((prefill_kernel<D, GH, BIG_BLOCKS>), grid, dim3(256), 0, stream,
                      (__bf16*)a.out, (const __bf16*)a.q, (const __bf16*)a.k_cache,
                      (const __bf16*)a.v_cache, a.num_blocks, a.block_tables,
                      a.max_blocks_per_seq, a.cu_seqlens_q, a.cu_seqlens_k, a.num_heads,
-                     a.num_kv_heads, bs_log2, a.scale * kLog2e, a.num_seqs, (int32_t)n_units,
-                     slot);
+                     a.num_kv_heads, bs_log2, a.scale * kLog2e);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
