@@ -46,19 +46,13 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Reductions over the four lanes l, l^16, l^32, l^48 (the 16-lane rows of a wavefront) with
+// Max over the four lanes l, l^16, l^32, l^48 (the 16-lane rows of a wavefront) with
 // v_permlane16_swap / v_permlane32_swap: VALU lane exchanges, no LDS round trip.
 __device__ __forceinline__ float rows_max(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
-}
-__device__ __forceinline__ float rows_sum(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left free) through the builtin, so the compiler's own
@@ -247,11 +241,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     for (int i = 0; i < DT; ++i)
   #pragma unroll
       for (int nt = 0; nt < GH; ++nt) oacc[i][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run[GH], l_run[GH];
+    // l_acc[nt]: the softmax denominators, accumulated by the PV MFMA with an all-ones A
+    // operand (every lane ends with its column's sum over the keys of the probabilities it
+    // fed to the PV product, bf16-rounded like them)
+    float m_run[GH];
+    f32x4_t l_acc[GH];
   #pragma unroll
     for (int nt = 0; nt < GH; ++nt) {
       m_run[nt] = -INFINITY;
-      l_run[nt] = 0.f;
+      l_acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
     int cblk[NL];
@@ -323,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
             const float m_new = fmaxf(m_run[nt], mxs[nt]);
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
             const float alpha = __builtin_amdgcn_exp2f((m_run[nt] - m_use) * scale_log2e);
-            l_run[nt] *= alpha;
+            l_acc[nt] *= alpha;
   #pragma unroll
             for (int i = 0; i < DT; ++i) oacc[i][nt] *= alpha;
             m_run[nt] = m_new;
@@ -332,17 +330,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   #pragma unroll
         for (int nt = 0; nt < GH; ++nt) {
           const float mc = (m_run[nt] == -INFINITY ? 0.f : m_run[nt]) * scale_log2e;
-          float psum = 0.f;
           float pv[4][4];
   #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
   #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mt][nt][r], scale_log2e, -mc));
-              pv[mt][r] = e;
-              psum += e;
-            }
-          l_run[nt] += psum;
+            for (int r = 0; r < 4; ++r)
+              pv[mt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][nt][r], scale_log2e, -mc));
   #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             u32x4_t w;
@@ -383,6 +376,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   #pragma unroll
           for (int nt = 0; nt < GH; ++nt) oacc[i][nt] = mfma16(av, pb[ks][nt], oacc[i][nt]);
         }
+      const bf16x8_t ones = __builtin_bit_cast(
+          bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+  #pragma unroll
+        for (int nt = 0; nt < GH; ++nt) l_acc[nt] = mfma16(ones, pb[ks][nt], l_acc[nt]);
     };
     for (int kt = 0; kt < n_kt; kt += 2) {
       tile_step(kt, lds_a, lds_b);
@@ -392,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     // normalise and store: lane holds dims 16 i + 4 quad + r of its query column
   #pragma unroll
     for (int nt = 0; nt < GH; ++nt) {
-      const float inv = 1.f / rows_sum(l_run[nt]);
+      const float inv = 1.f / l_acc[nt][0];
       if (row_ok) {
         __bf16* orow = out + ((int64_t)(q_begin + i_row) * num_heads + h0 + nt) * D;
   #pragma unroll
