@@ -177,7 +177,10 @@ int paged_attn_decode(void* out, const void* q,
  * Preconditions: cu_seqlens_q[num_seqs] == total_q; Lq <= max_seqlen_q (rows past it are
  * left unwritten); Lk >= Lq; Lk <= max_blocks_per_seq * bs (larger Lk is clamped); table
  * entries below ceil(Lk / bs) lie in [0, num_blocks) - an entry outside it is not
- * dereferenced and turns that sequence's output rows into NaN.
+ * dereferenced; it turns into NaN every output row of that sequence that attends a key in
+ * that block, and may do the same to other rows of that sequence sharing a 64-row query
+ * tile with one (tiles are counted back from the sequence's last row). Rows of other
+ * sequences are unaffected.
  * Supported: bf16 only (fp32 accumulation); D in {64, 128}; G in {1, 2, 4, 8}; bs a power
  * of two >= 16. Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.
  * -------------------------------------------------------------------------------------*/

@@ -117,3 +117,21 @@ def test_decode_equals_one_query_prefill_across_entry_points():
 def test_prefill_empty_sequences_in_batch():
     w = make_prefill(314, [0, 90, 0, 5], cached=[10, 0, 0, 300], Hq=16, Hkv=8, D=128, bs=256)
     check(w)
+
+
+def test_prefill_invalid_block_id_poisons_only_rows_that_reach_it():
+    # seq 0: bad third block (keys 512..639) - rows 0..511 never reach it, rows 512..639 do;
+    # seq 1: bad cached-prefix block - every row attends it; seq 2 untouched.
+    w = make_prefill(312, [640, 300, 200], cached=[0, 256, 40], Hq=16, Hkv=8, D=128, bs=256)
+    ds = DeviceStep(w)
+    ds.store()
+    ds.block_tables[0, 2] = w.num_blocks + 3      # out of range: must not be read
+    ds.block_tables[1, 0] = -7
+    ds.attend()
+    torch.cuda.synchronize()
+    out = ds.out_f64()
+    ref, _, _, _ = run_workload(w)
+    assert np.all(np.isnan(out[512:640]))
+    assert np.all(np.isnan(out[640:940]))
+    keep = np.r_[0:512, 940:1140]
+    assert_attention_close(out[keep], ref[keep], rel_l2=1e-2, label="unaffected rows")
