@@ -170,19 +170,23 @@ int paged_attn_decode(void* out, const void* q,
  *   k_cache, v_cache  device [num_blocks, bs, Hkv, D] bf16 (the new tokens already stored)
  *   block_tables device int32 [num_seqs, max_blocks_per_seq]
  *   cu_seqlens_q, cu_seqlens_k  device int32 [num_seqs + 1]
- *   max_seqlen_q host int: an upper bound of every Lq (sizes the launch, as in the
- *                engine's Context); max_seqlen_k is accepted for the same interface.
+ *   max_seqlen_q, max_seqlen_k  host ints: upper bounds of every Lq and every Lk (the
+ *                engine's Context carries both); max_seqlen_k sizes the launch, which has
+ *                one plane of workgroups per possible count of 64-key tiles.
  *   causal       must be 1 (the engine always attends causally).
  * out, q, k_cache and v_cache must be 16-byte aligned (PKV_ERR_INVALID otherwise).
- * Preconditions: cu_seqlens_q[num_seqs] == total_q; Lq <= max_seqlen_q (rows past it are
- * left unwritten); Lk >= Lq; Lk <= max_blocks_per_seq * bs (larger Lk is clamped); table
- * entries below ceil(Lk / bs) lie in [0, num_blocks) - an entry outside it is not
+ * Preconditions: cu_seqlens_q[num_seqs] == total_q; Lq <= max_seqlen_q; Lk >= Lq;
+ * Lk <= max_seqlen_k (a sequence breaking this may have rows left unwritten);
+ * Lk <= max_blocks_per_seq * bs (larger Lk is clamped); table entries below
+ * ceil(Lk / bs) lie in [0, num_blocks) - an entry outside it is not
  * dereferenced; it turns into NaN every output row of that sequence that attends a key in
  * that block, and may do the same to other rows of that sequence sharing a 64-row query
  * tile with one (tiles are counted back from the sequence's last row). Rows of other
  * sequences are unaffected.
  * Supported: bf16 only (fp32 accumulation); D in {64, 128}; G in {1, 2, 4, 8}; bs a power
- * of two >= 16. Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.
+ * of two >= 16; num_seqs <= 65535 and ceil(min(max_seqlen_k, max_blocks_per_seq * bs) / 64)
+ * <= 65535. Errors: PKV_ERR_INVALID (also max_seqlen_k < max_seqlen_q),
+ * PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.
  * -------------------------------------------------------------------------------------*/
 int paged_attn_prefill_varlen(void* out, const void* q,
                               const void* k_cache, const void* v_cache, int32_t num_blocks,

@@ -246,17 +246,20 @@ int paged_attn_prefill_varlen(void* out, const void* q, const void* k_cache, con
                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                               float scale, int32_t causal, pkv_dtype_t dtype,
                               hipStream_t stream) {
-  (void)max_seqlen_k;
   if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
   if (causal != 1) return PKV_ERR_UNSUPPORTED;
   if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || num_blocks < 0 || max_blocks_per_seq <= 0)
     return PKV_ERR_INVALID;
+  if (max_seqlen_k < max_seqlen_q) return PKV_ERR_INVALID;  // every Lk >= its Lq
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return PKV_ERR_INVALID;
   if (!pow2_at_least_16(block_size)) return PKV_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (!supported_group(num_heads, num_kv_heads)) return PKV_ERR_UNSUPPORTED;
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PKV_ERR_INVALID;
-  if (num_seqs > 65535 || ceil_div(max_seqlen_q, 64) > 65535) return PKV_ERR_UNSUPPORTED;
+  // the launch has one plane per possible count of 64-key tiles of a unit
+  const int64_t key_cap = (int64_t)max_blocks_per_seq * block_size;
+  const int64_t key_tiles = ((max_seqlen_k < key_cap ? max_seqlen_k : key_cap) + 63) / 64;
+  if (num_seqs > 65535 || key_tiles > 65535) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens_q || !cu_seqlens_k)
     return PKV_ERR_INVALID;
@@ -273,7 +276,7 @@ int paged_attn_prefill_varlen(void* out, const void* q, const void* k_cache, con
   a.cu_seqlens_q = cu_seqlens_q;
   a.cu_seqlens_k = cu_seqlens_k;
   a.num_seqs = num_seqs;
-  a.max_seqlen_q = max_seqlen_q;
+  a.key_tiles = (int32_t)key_tiles;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;

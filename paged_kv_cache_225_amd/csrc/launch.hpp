@@ -46,7 +46,8 @@ struct PrefillArgs {
   int32_t max_blocks_per_seq;
   const int32_t* cu_seqlens_q;
   const int32_t* cu_seqlens_k;
-  int32_t num_seqs, max_seqlen_q;
+  int32_t num_seqs;
+  int32_t key_tiles;         // grid planes: ceil(min(max_seqlen_k, table capacity) / 64)
   int32_t num_heads, num_kv_heads, head_dim, block_size;
   float scale;
 };

@@ -7,8 +7,8 @@
 // K=[ABCDEF]) are visible to every query.
 //
 // Work unit: (q-head group of GH heads sharing one kv head, sequence b, 64 query positions).
-// Units are numbered from the end of each sequence so the longest rows (most keys) are
-// dispatched first. Each of the 4 wavefronts owns 16 query positions x GH heads.
+// Units are dispatched longest first (most 64-key tiles) so that short units fill the slots
+// the long ones leave. Each of the 4 wavefronts owns 16 query positions x GH heads.
 //
 // Key tiles of 64 keys go from HBM straight into LDS with global_load_lds_dwordx4 (no
 // register staging), double-buffered: the loads of tile t+1 are issued right after the
@@ -89,11 +89,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   __shared__ __attribute__((aligned(1024))) char lds_a[2][TILEB];  // [K=0,V=1]
   __shared__ __attribute__((aligned(1024))) char lds_b[2][TILEB];
 
-  // Work unit: (head group hg, sequence b, query tile t counted from the sequence end) =
-  // (blockIdx.x, blockIdx.y, blockIdx.z). x = hg runs fastest, so the workgroups of a head
-  // group - dealt round-robin to the XCDs - stay on one XCD, where all its query tiles share
-  // the K/V in L2; z = t puts the longest rows (most keys) first.
-  auto unit = [&](const int hg, const int b, const int t) {
+  // Work unit: (head group hg, sequence b, query tile t counted from the sequence end); it
+  // reads ceil(Lk / 64) - t key tiles. blockIdx.x = hg runs fastest, so the workgroups of a
+  // head group - dealt round-robin to the XCDs - stay on one XCD, where all its query tiles
+  // share the K/V in L2. Plane z = blockIdx.z holds, for each sequence, the unit with
+  // exactly nkt = gridDim.z - z key tiles, if the sequence has one: the dispatcher, which
+  // hands workgroups out in index order, starts the longest units first. Within a plane the
+  // sequences are rotated by z: consecutive workgroups go round-robin to the shader
+  // engines of an XCD, and unrotated a sequence would meet the same engine in every plane,
+  // leaving the engines that drew the long sequences with most of the work.
+  auto unit = [&](const int hg, const int b, const int z) {
     const int G = num_heads / num_kv_heads;
     const int h0 = hg * GH, g = h0 / G;
     const int q_begin = cu_q[b];
@@ -101,6 +106,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     const int cap = bt_stride << bs_log2;
     int Lk = cu_k[b + 1] - cu_k[b];
     Lk = Lk > cap ? cap : Lk;
+    const int t = (Lk + kBK - 1) / kBK - ((int)gridDim.z - z);
+    if (t < 0) return;              // no unit of this length in this sequence
     const int i_hi = Lq - kBQ * t;  // exclusive end of this unit's query rows
     if (i_hi <= 0) return;
     const int i_lo = i_hi - kBQ;    // may be negative: those rows are idle
@@ -404,14 +411,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       }
     }
   };
-  unit(blockIdx.x, blockIdx.y, blockIdx.z);
+  const int B = gridDim.y, z = blockIdx.z;
+  int b = blockIdx.y + z % B;
+  if (b >= B) b -= B;
+  unit(blockIdx.x, b, z);
 }
 
 template <int D, int GH, bool BIG_BLOCKS>
 static int run_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int bs_log2 = __builtin_ctz((unsigned)a.block_size);
-  const int n_tiles = (a.max_seqlen_q + kBQ - 1) / kBQ;
-  dim3 grid(a.num_heads / GH, a.num_seqs, n_tiles);
+  dim3 grid(a.num_heads / GH, a.num_seqs, a.key_tiles);
   hipLaunchKernelGGL((prefill_kernel<D, GH, BIG_BLOCKS>), grid, dim3(256), 0, stream,
                      (__bf16*)a.out, (const __bf16*)a.q, (const __bf16*)a.k_cache,
                      (const __bf16*)a.v_cache, a.num_blocks, a.block_tables,
@@ -426,7 +435,7 @@ static int run_prefill_bs(const PrefillArgs& a, hipStream_t stream) {
 }
 
 int launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  if (a.num_seqs == 0 || a.max_seqlen_q == 0) return 0;
+  if (a.num_seqs == 0 || a.key_tiles == 0) return 0;
   const int G = a.num_heads / a.num_kv_heads;
   const bool pair = (G % 2) == 0;
   if (a.head_dim == 128) return pair ? run_prefill_bs<128, 2>(a, stream) : run_prefill_bs<128, 1>(a, stream);

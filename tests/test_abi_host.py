@@ -153,6 +153,8 @@ def test_decode_argument_validation(kw, status):
     (dict(bs=100), -2), (dict(q=None), -1), (dict(B=0), 0), (dict(T=0), 0), (dict(mq=0), 0),
     (dict(out=ctypes.c_void_p(0x1002)), -1), (dict(q=ctypes.c_void_p(0x1008)), -1),
     (dict(k=ctypes.c_void_p(0x1004)), -1), (dict(v=ctypes.c_void_p(0x100c)), -1),
+    # max_seqlen_k bounds every Lk >= Lq, and sizes the launch (one plane per 64-key count)
+    (dict(mk=7), -1), (dict(mk=-1, mq=0), -1), (dict(W=65536, mk=1 << 23), -2),
 ])
 def test_prefill_argument_validation(kw, status):
     assert _prefill_rc(**kw) == status

@@ -135,3 +135,19 @@ def test_prefill_invalid_block_id_poisons_only_rows_that_reach_it():
     assert np.all(np.isnan(out[640:940]))
     keep = np.r_[0:512, 940:1140]
     assert_attention_close(out[keep], ref[keep], rel_l2=1e-2, label="unaffected rows")
+
+
+def test_prefill_loose_max_seqlen_k_is_bitwise_identical():
+    # a larger max_seqlen_k only adds planes of empty workgroups to the launch
+    w = make_prefill(313, [333, 0, 64, 17, 900], cached=[40, 5, 0, 300, 100], Hq=16, Hkv=8,
+                     D=128, bs=64)
+    ds = gpu_run(w)
+    a = ds.out.clone()
+    ds.out.view(torch.int16).fill_(0x7FC0)
+    B.paged_attn_prefill_varlen(ds.out, ds.q, ds.k_cache, ds.v_cache, ds.block_tables,
+                                ds.cu_seqlens_q, ds.cu_seqlens_k, ds.max_seqlen_q,
+                                ds.max_seqlen_k + 777, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), ds.out.view(torch.int16))
+    ref, _, _, _ = run_workload(w)
+    assert_attention_close(ds.out_f64(), ref, rel_l2=1e-2, label="loose bound")
