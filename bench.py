@@ -2,8 +2,10 @@
 
 Headline: one engine step of the Qwen3-0.6B-shaped decode workload (batch 64, 16 q heads /
 8 kv heads, head_dim 128, bf16, context U[256, 4096], block 256, 2048-block pool): store
-the 64 new tokens' K/V with store_kvcache, then paged_attn_decode (split-K partials + the
-combine). Consecutive steps rotate over several layer pools (each a full copy of the
+the 64 new tokens' K/V and attend, as one paged_attn_decode_store call (split-K partials,
+then the combine, which also writes the new rows into their slots). The same step as the
+two separate calls (store_kvcache, then paged_attn_decode) is timed after it and reported
+beside it. Consecutive steps rotate over several layer pools (each a full copy of the
 2048-block K/V pool, as every layer of the engine owns its own cache), so the KV read
 streams from HBM rather than from the 256 MB last-level cache.
 
@@ -87,35 +89,41 @@ def bench_decode_headline(torch, args):
     stream = torch.cuda.current_stream()
     from paged_kv_cache_225_amd import _binding as B
 
-    def step(i):
+    def fused(i):
+        kc, vc = layers[i % len(layers)]
+        B.paged_attn_decode_store(base.out, base.q, base.new_k, base.new_v, base.slot_mapping,
+                                  kc, vc, base.block_tables, base.context_lens, w.scale,
+                                  workspace=base.workspace, stream=stream)
+
+    def separate(i):
         kc, vc = layers[i % len(layers)]
         B.store_kvcache(base.new_k, base.new_v, kc, vc, base.slot_mapping, stream=stream)
         B.paged_attn_decode(base.out, base.q, kc, vc, base.block_tables, base.context_lens,
                             w.scale, workspace=base.workspace, stream=stream)
 
-    for i in range(args.warmup):
-        step(i)
-    # timed region: exactly K steps between two synchronisations; the decode call of each
-    # step is bracketed by events on the launch stream for the per-launch kernel time
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        kc, vc = layers[i % len(layers)]
-        B.store_kvcache(base.new_k, base.new_v, kc, vc, base.slot_mapping, stream=stream)
-        ev[i][0].record(stream)
-        B.paged_attn_decode(base.out, base.q, kc, vc, base.block_tables, base.context_lens,
-                            w.scale, workspace=base.workspace, stream=stream)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        # exactly K steps between two synchronisations; each call is bracketed by events on
+        # the launch stream for the per-launch kernel time
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            fn(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        return elapsed * 1e3 / args.steps, np.array([a.elapsed_time(b) for a, b in ev])
+
+    ms_per_step, call_ms = timed(fused)
+    sep_ms_per_step, sep_call_ms = timed(separate)
     step_bytes_dec, kv = decode_bytes(w)
     step_bytes = step_bytes_dec + store_bytes(w)
-    ms_per_step = elapsed * 1e3 / args.steps
-    dec_avg = float(dec_ms.mean())
-    achieved = step_bytes_dec / (dec_avg * 1e-3) / 1e9
+    call_avg = float(call_ms.mean())
+    achieved = step_bytes / (call_avg * 1e-3) / 1e9
     return {
         "w": w,
         "name": CONFIG_NAMES[2],
@@ -124,9 +132,12 @@ def bench_decode_headline(torch, args):
         "tokens_per_s": w.num_seqs / (ms_per_step * 1e-3),
         "step_bytes": step_bytes,
         "kv_bytes": kv,
-        "decode_call_us_avg": dec_avg * 1e3,
-        "decode_call_us_p10_p90": [float(np.percentile(dec_ms, 10)) * 1e3,
-                                   float(np.percentile(dec_ms, 90)) * 1e3],
+        "decode_call_us_avg": call_avg * 1e3,
+        "decode_call_us_p10_p90": [float(np.percentile(call_ms, 10)) * 1e3,
+                                   float(np.percentile(call_ms, 90)) * 1e3],
+        "separate_calls": {"ms_per_step": sep_ms_per_step,
+                           "value": step_bytes / (sep_ms_per_step * 1e-3) / 1e9,
+                           "call_us_avg": float(sep_call_ms.mean()) * 1e3},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": decode_traffic_bytes()},
     }
@@ -286,11 +297,12 @@ def main():
         "config": {"workload": head["name"], "global_batch": 64, "heads_q": 16, "heads_kv": 8,
                    "head_dim": 128, "block_size": 256, "pool_blocks": 2048,
                    "context": "uniform[256,4096]", "layer_pools_rotated": args.layers,
-                   "step": "store_kvcache(64 tokens) + paged_attn_decode"},
+                   "step": "paged_attn_decode_store: store of the 64 new tokens' K/V + decode attention, one call"},
         "roofline": head["roofline"],
         "tokens_per_s": head["tokens_per_s"],
         "decode_call_us_avg": head["decode_call_us_avg"],
         "decode_call_us_p10_p90": head["decode_call_us_p10_p90"],
+        "separate_calls": head["separate_calls"],
         "step_bytes": head["step_bytes"],
         "kv_bytes": head["kv_bytes"],
         "host_metadata_us": host_metadata_us(w),

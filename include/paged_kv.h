@@ -158,6 +158,38 @@ int paged_attn_decode(void* out, const void* q,
                       hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * Decode attention with the step's store fused in - [P1] Attention.forward, decode branch:
+ * store_kvcache of the step's K/V rows, then the decode attention over the cache.
+ * Same result as store_kvcache(key, value, k_cache, v_cache, slot_mapping[0 .. num_seqs))
+ * followed by paged_attn_decode(...) with the same arguments, up to rounding: token b of
+ * key / value is the newest token of sequence b (position context_lens[b] - 1), so the
+ * attention takes that token's K/V from key / value and the other context_lens[b] - 1
+ * keys from the cache, and the rows are written to slot slot_mapping[b] of the caches
+ * (bit for bit; -1 or a slot >= num_blocks * block_size is skipped) within the call.
+ *   key, value   device [num_seqs, Hkv, D], dtype, token stride *_token_stride elements
+ *                (>= Hkv * D; stride * element size a multiple of 16 bytes), 16-byte aligned.
+ *   slot_mapping device int32 [num_seqs] ([P1] prepare_decode's slot of the newest token).
+ *   Other arguments, the workspace and its size: as paged_attn_decode.
+ * Preconditions: those of paged_attn_decode and store_kvcache; slot_mapping[b] is the slot
+ * of position context_lens[b] - 1 in sequence b's block table (then the cache ends up as
+ * after the two separate calls). Sequences with context_lens[b] == 0 get a zero row; their
+ * rows are still stored if their slot is valid.
+ * Errors: as paged_attn_decode, plus PKV_ERR_INVALID for null key / value / slot_mapping
+ * or a stride or alignment outside the rules above.
+ * -------------------------------------------------------------------------------------*/
+int paged_attn_decode_store(void* out, const void* q,
+                            const void* key, int64_t key_token_stride,
+                            const void* value, int64_t value_token_stride,
+                            const int32_t* slot_mapping,
+                            void* k_cache, void* v_cache, int32_t num_blocks,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, float scale, pkv_dtype_t dtype,
+                            int32_t partition_size, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * Varlen causal prefill - [P1] Attention.forward (prefill branch, flash_attn_varlen_func
  * with block_table, causal=True); [P1] prepare_prefill for cu_seqlens; [P2] 请求执行 –
  * 输入序列预处理与context构建 for prefix-cache hits (keys cover more tokens than queries).

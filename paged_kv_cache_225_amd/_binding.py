@@ -35,6 +35,9 @@ SIGNATURES = {
     "paged_attn_decode_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "paged_attn_decode": (_c_int, [_p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32,
                                    _i32, _f, _c_int, _i32, _p, _size, _p]),
+    "paged_attn_decode_store": (_c_int, [_p, _p, _p, _i64, _p, _i64, _p, _p, _p, _i32, _p, _i32,
+                                         _p, _i32, _i32, _i32, _i32, _i32, _f, _c_int, _i32, _p,
+                                         _size, _p]),
     "paged_attn_prefill_varlen": (_c_int, [_p, _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32,
                                            _i32, _i32, _i32, _i32, _i32, _i32, _f, _i32, _c_int,
                                            _p]),
@@ -192,6 +195,25 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
         _t_ptr(block_tables), W, _t_ptr(context_lens), B, Hq, Hkv, D, bs, float(scale),
         _dtype_code(q), partition_size, _t_ptr(workspace), ws_bytes, _stream(stream))
     _check("paged_attn_decode", rc)
+
+
+def paged_attn_decode_store(out, q, key, value, slot_mapping, k_cache, v_cache, block_tables,
+                            context_lens, scale, workspace=None, partition_size=0, stream=None):
+    """paged_attn_decode with the step's store fused in: key/value [B, Hkv, D] (token stride
+    free, head stride D, unit element stride) are the newest tokens' rows, written to
+    slot_mapping int32 [B]; other arguments as paged_attn_decode."""
+    B, Hq, D = q.shape
+    num_blocks, bs, Hkv, _ = k_cache.shape
+    if key.stride(2) != 1 or key.stride(1) != D or value.stride(2) != 1 or value.stride(1) != D:
+        raise ValueError("key/value need head stride head_dim and unit element stride")
+    W = block_tables.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().paged_attn_decode_store(
+        _t_ptr(out), _t_ptr(q), _t_ptr(key), key.stride(0), _t_ptr(value), value.stride(0),
+        _t_ptr(slot_mapping), _t_ptr(k_cache), _t_ptr(v_cache), num_blocks,
+        _t_ptr(block_tables), W, _t_ptr(context_lens), B, Hq, Hkv, D, bs, float(scale),
+        _dtype_code(q), partition_size, _t_ptr(workspace), ws_bytes, _stream(stream))
+    _check("paged_attn_decode_store", rc)
 
 
 def paged_attn_prefill_varlen(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k,

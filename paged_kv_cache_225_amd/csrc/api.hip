@@ -178,12 +178,19 @@ size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, in
   return partials + meta;
 }
 
-int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                      int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                      const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
-                      pkv_dtype_t dtype, int32_t partition_size, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The shared body of paged_attn_decode and paged_attn_decode_store (fused: the latter).
+int decode_common(void* out, const void* q, const void* k_cache, const void* v_cache,
+                  int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                  pkv_dtype_t dtype, int32_t partition_size, void* workspace,
+                  size_t workspace_bytes, bool fused, const void* key,
+                  int64_t key_token_stride, const void* value, int64_t value_token_stride,
+                  const int32_t* slot_mapping, hipStream_t stream) {
   if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_blocks < 1 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID;
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return PKV_ERR_INVALID;
@@ -198,8 +205,15 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
   int64_t max_parts;
   if (decode_parts(max_blocks_per_seq, block_size, partition_size, &part, &max_parts) != PKV_OK)
     return PKV_ERR_INVALID;
+  const int elem = dtype == PKV_BF16 ? 2 : 4;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (fused) {
+    if (key_token_stride < row || value_token_stride < row) return PKV_ERR_INVALID;
+    if ((key_token_stride * elem) % 16 || (value_token_stride * elem) % 16) return PKV_ERR_INVALID;
+  }
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_INVALID;
+  if (fused && (!key || !value || !slot_mapping)) return PKV_ERR_INVALID;
   const size_t need = paged_attn_decode_workspace_bytes(num_seqs, num_heads, head_dim,
                                                         max_blocks_per_seq, block_size,
                                                         partition_size);
@@ -207,6 +221,7 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
       !aligned16(workspace))
     return PKV_ERR_INVALID;
+  if (fused && (!aligned16(key) || !aligned16(value))) return PKV_ERR_INVALID;
   pkv::DecodeArgs a;
   a.out = out;
   a.q = q;
@@ -233,8 +248,45 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
   }
   a.ws_ml = (float*)workspace + (size_t)num_seqs * num_heads * max_parts * head_dim;
   a.ws_meta = (int32_t*)(a.ws_ml + (size_t)num_seqs * num_heads * max_parts * 2);
+  a.new_k = fused ? key : nullptr;  // the kernels key the fused path on new_k
+  a.new_k_stride = key_token_stride;
+  a.new_v = value;
+  a.new_v_stride = value_token_stride;
+  a.slot_mapping = slot_mapping;
+  a.num_slots = (int64_t)num_blocks * block_size;
   const int rc = pkv::launch_decode(a, stream);
   return rc == 0 ? PKV_OK : (rc == -2 ? PKV_ERR_UNSUPPORTED : PKV_ERR_HIP);
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                      pkv_dtype_t dtype, int32_t partition_size, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return decode_common(out, q, k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       scale, dtype, partition_size, workspace, workspace_bytes, false, nullptr,
+                       0, nullptr, 0, nullptr, stream);
+}
+
+int paged_attn_decode_store(void* out, const void* q, const void* key, int64_t key_token_stride,
+                            const void* value, int64_t value_token_stride,
+                            const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                            int32_t num_blocks, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, float scale, pkv_dtype_t dtype,
+                            int32_t partition_size, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  return decode_common(out, q, k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       scale, dtype, partition_size, workspace, workspace_bytes, true, key,
+                       key_token_stride, value, value_token_stride, slot_mapping, stream);
 }
 
 // ------------------------------------------------------------------------- prefill

@@ -27,6 +27,13 @@
 //   M = max_p m_p, L = sum_p 2^(m_p - M) l_p, out = sum_p 2^(m_p - M) o_p / L.
 // Keys past the context length are never loaded, so block-table padding and the unused
 // (possibly NaN) slots of a sequence's last block are not touched.
+//
+// Fused store (the store_kvcache that precedes decode attention in the engine's
+// Attention.forward): the stream kernel takes n_b - 1 keys of each sequence from the cache
+// and always writes partials; the combine kernel adds the newest token as one more piece,
+// (m, l, o) = (scale <q, k_new>, 1, v_new) straight from the step's key/value rows, and its
+// first wavefront of each kv head copies those rows into their slots. No kernel of the call
+// reads the newest token's slot, so the copy needs no ordering against the attention.
 #include <math.h>
 
 #include "common.hpp"
@@ -58,7 +65,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     int32_t bt_stride, const int32_t* __restrict__ context_lens, int32_t num_seqs,
     int32_t num_kv_heads, int32_t bs_log2, float scale_log2e, int32_t min_keys,
     int32_t max_pieces, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-    int32_t* __restrict__ ws_meta) {
+    int32_t* __restrict__ ws_meta, int32_t skip_last) {
   using E = Elem<T>;
   constexpr bool kBF16 = E::kBytes == 2;
   constexpr int EPL = E::kPerChunk;  // elements per 16-byte lane chunk
@@ -79,6 +86,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     for (int base = 0; base < num_seqs; base += 64) {
       const int b = base + threadIdx.x;
       int v = b < num_seqs ? clamp_ctx(context_lens[b], cap) : 0;
+      v -= skip_last & (v > 0);  // the newest token comes from the step's rows
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const int t = __shfl_up(v, off);
@@ -274,7 +282,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
       l[h] = lt;
     }
     if (rsub == 0) {
-      const bool whole = piece_x0 == c.seg_start && c.x + c.cnt == c.seg_start + c.n;
+      const bool whole = !skip_last && piece_x0 == c.seg_start && c.x + c.cnt == c.seg_start + c.n;
       if (whole) {
         T* dst0 = out + ((int64_t)c.b * Hq + c.g * G) * D + sub * EPL;
 #pragma unroll
@@ -347,26 +355,47 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   }
 }
 
+// D / 64 elements of one row per lane, as raw bits (a copy) or as floats.
+template <typename T, int DPL> struct LaneBits;
+template <> struct LaneBits<__bf16, 1> { typedef uint16_t type; };
+template <> struct LaneBits<__bf16, 2> { typedef uint32_t type; };
+template <> struct LaneBits<float, 1> { typedef uint32_t type; };
+template <> struct LaneBits<float, 2> { typedef u32x2_t type; };
+template <typename T, int DPL>
+__device__ __forceinline__ void bits_to_float(const typename LaneBits<T, DPL>::type& w, float* f) {
+  if constexpr (Elem<T>::kBytes == 2) {
+    if constexpr (DPL == 2) { f[0] = bf16_lo(w); f[1] = bf16_hi(w); }
+    else f[0] = __uint_as_float((uint32_t)w << 16);
+  } else {
+    if constexpr (DPL == 2) { f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y); }
+    else f[0] = __uint_as_float(w);
+  }
+}
+
 // Merges the partial slots of every (sequence, query head) whose segment was split: one
 // wavefront per (sequence, head), four per workgroup. The kernel is latency bound, so it
 // takes two rounds of loads: first the split metadata together with the (m, l) of the
 // first 64 slots (lane p holds slot p; the slots exist for every row, so they are read
-// before the row's slot count is known), then the o rows of up to 16 slots at a time,
-// D / 64 consecutive floats per lane (one coalesced row per load instruction).
+// before the row's slot count is known) and, for the fused store, q and the newest token's
+// rows; then the o rows of up to 16 slots at a time, D / 64 consecutive floats per lane
+// (one coalesced row per load instruction).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     T* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t cap,
     int32_t num_rows, int32_t Hq, int32_t Hkv, int32_t max_pieces,
     const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
-    const int32_t* __restrict__ ws_meta, int32_t per_seq_line) {
+    const int32_t* __restrict__ ws_meta, int32_t per_seq_line, NewTokens nt) {
   constexpr int DPL = D / 64;  // floats per lane
   constexpr int OB = 16;       // o rows per load batch
   static_assert(DPL == 1 || DPL == 2, "head_dim 64 or 128");
+  typedef typename LaneBits<T, DPL>::type Bits;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // b * Hq + h
   if (row >= num_rows) return;
   const int b = row / Hq, h = row - b * Hq;
+  const int g = h / (Hq / Hkv);
   const int64_t base = (int64_t)row * max_pieces;
+  const bool fused = nt.key != nullptr;
   // round 1
   const int n_raw = context_lens[b];
   const int S = ws_meta[0];
@@ -376,20 +405,28 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     mp = ws_ml[2 * (base + lane)];
     lp = ws_ml[2 * (base + lane) + 1];
   }
+  Bits qw{}, kw{}, vw{};
+  int slot = -1;
+  if (fused) {
+    const int64_t col = (int64_t)g * D + lane * DPL;
+    qw = *reinterpret_cast<const Bits*>(reinterpret_cast<const T*>(nt.q) + (int64_t)row * D + lane * DPL);
+    kw = *reinterpret_cast<const Bits*>(reinterpret_cast<const T*>(nt.key) + b * nt.key_stride + col);
+    vw = *reinterpret_cast<const Bits*>(reinterpret_cast<const T*>(nt.value) + b * nt.value_stride + col);
+    slot = nt.slot_mapping[b];
+  }
   const int n = clamp_ctx(n_raw, cap);
+  const int nc = fused ? n - (n > 0) : n;  // keys the stream kernel took from the cache
   T* dst = out + (int64_t)row * D + lane * DPL;
   float acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-  float L = 1.f;  // a sequence with context length 0 gets a zero row
-  if (n > 0) {
-    const int g = h / (Hq / Hkv);
+  float M = -INFINITY;
+  float L = 0.f;
+  if (nc > 0) {
     // start of the segment on the split line: one per (sequence, kv head), or one per sequence
-    const int seg_start = per_seq_line ? cum : Hkv * cum + g * n;
-    const int np = (seg_start + n - 1) / S - seg_start / S + 1;
-    if (np == 1) return;  // written by the stream kernel
-    float M = -INFINITY;
-    L = 0.f;
+    const int seg_start = per_seq_line ? cum : Hkv * cum + g * nc;
+    const int np = (seg_start + nc - 1) / S - seg_start / S + 1;
+    if (np == 1 && !fused) return;  // written by the stream kernel
     for (int p0 = 0; p0 < np; p0 += 64) {
       const int cnt = min(64, np - p0);
       if (p0 > 0) {  // slots past the first 64 (segments cut into more than 64 pieces)
@@ -434,6 +471,31 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
       }
     }
   }
+  if (fused) {
+    if (n > 0) {  // the newest token as one more piece: m = scale <q, k>, l = 1, o = v
+      float qf[DPL], kf[DPL], vf[DPL];
+      bits_to_float<T, DPL>(qw, qf);
+      bits_to_float<T, DPL>(kw, kf);
+      bits_to_float<T, DPL>(vw, vf);
+      float sd = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) sd = fmaf(qf[e], kf[e], sd);
+      const float ms = group_sum<64>(sd) * nt.scale_log2e;
+      const float Mn = fmaxf(M, ms);
+      const float rescale = __builtin_amdgcn_exp2f(M - Mn);
+      const float wn = __builtin_amdgcn_exp2f(ms - Mn);
+      L = fmaf(L, rescale, wn);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(acc[e], rescale, wn * vf[e]);
+    }
+    // one wavefront per kv head stores the step's K/V rows (bit for bit) into their slot
+    if (h % (Hq / Hkv) == 0 && slot >= 0 && (int64_t)slot < nt.num_slots) {
+      const int64_t off = (int64_t)slot * Hkv * D + (int64_t)g * D + lane * DPL;
+      *reinterpret_cast<Bits*>(reinterpret_cast<T*>(nt.k_cache) + off) = kw;
+      *reinterpret_cast<Bits*>(reinterpret_cast<T*>(nt.v_cache) + off) = vw;
+    }
+  }
+  if (n == 0) L = 1.f;  // a sequence with context length 0 gets a zero row
   const float inv = 1.f / L;
   if constexpr (DPL == 2) {
     if constexpr (Elem<T>::kBytes == 2) {
@@ -462,11 +524,22 @@ static int run_decode(const DecodeArgs& a, hipStream_t stream) {
                      lds, stream, (T*)a.out, (const T*)a.q, (const T*)a.k_cache,
                      (const T*)a.v_cache, a.num_blocks, a.block_tables, a.max_blocks_per_seq,
                      a.context_lens, a.num_seqs, a.num_kv_heads, bs_log2, c, a.partition,
-                     a.max_parts, a.ws_o, a.ws_ml, a.ws_meta);
+                     a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, a.new_k != nullptr ? 1 : 0);
   const int rows = a.num_seqs * a.num_heads;
+  NewTokens nt;
+  nt.q = a.q;
+  nt.key = a.new_k;
+  nt.key_stride = a.new_k_stride;
+  nt.value = a.new_v;
+  nt.value_stride = a.new_v_stride;
+  nt.slot_mapping = a.slot_mapping;
+  nt.k_cache = const_cast<void*>(a.k_cache);
+  nt.v_cache = const_cast<void*>(a.v_cache);
+  nt.num_slots = a.num_slots;
+  nt.scale_log2e = c;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256),
                      0, stream, (T*)a.out, a.context_lens, (int32_t)cap, rows, a.num_heads,
-                     a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, HPW > 0 ? 1 : 0);
+                     a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, HPW > 0 ? 1 : 0, nt);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

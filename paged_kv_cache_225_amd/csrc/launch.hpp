@@ -33,6 +33,28 @@ struct DecodeArgs {
   float* ws_ml;             // [num_seqs, Hq, max_parts, 2]
   int32_t* ws_meta;         // [num_seqs + 2]: the share size, then the context prefix sums
   int32_t max_workgroups;   // cap of the decode grid (4 wavefronts each)
+  // fused store of the step's tokens (new_k == nullptr: attention only); token b of
+  // new_k / new_v is the newest token of sequence b, written to slot slot_mapping[b]
+  const void* new_k;
+  int64_t new_k_stride;     // elements between tokens
+  const void* new_v;
+  int64_t new_v_stride;
+  const int32_t* slot_mapping;
+  int64_t num_slots;
+};
+
+// What the combine kernel needs for the fused store (key == nullptr: not fused).
+struct NewTokens {
+  const void* q;
+  const void* key;
+  int64_t key_stride;
+  const void* value;
+  int64_t value_stride;
+  const int32_t* slot_mapping;
+  void* k_cache;
+  void* v_cache;
+  int64_t num_slots;
+  float scale_log2e;
 };
 int launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -5,7 +5,8 @@ paged pool on the GPU poisoned with NaN (as the engine's ``torch.empty`` pool ho
 arbitrary bits), makes the resident tokens resident with the library's own metadata and
 ``store_kvcache``, and prepares the step's inputs. ``step()`` then runs the hot path:
 ``store_kvcache`` of the new tokens followed by ``paged_attn_decode`` or
-``paged_attn_prefill_varlen``. Host metadata is built by the library's host calls.
+``paged_attn_prefill_varlen``; ``step_fused()`` runs a decode step as one
+``paged_attn_decode_store`` call. Host metadata is built by the library's host calls.
 """
 from __future__ import annotations
 
@@ -122,6 +123,16 @@ class DeviceStep:
     def step(self, stream=None):
         self.store(stream)
         self.attend(stream)
+        return self.out
+
+    def step_fused(self, stream=None):
+        """Decode only: the same step through paged_attn_decode_store (one call)."""
+        w = self.w
+        assert w.kind == "decode"
+        B.paged_attn_decode_store(self.out, self.q, self.new_k, self.new_v, self.slot_mapping,
+                                  self.k_cache, self.v_cache, self.block_tables,
+                                  self.context_lens, w.scale, workspace=self.workspace,
+                                  partition_size=self.partition_size, stream=stream)
         return self.out
 
     def out_f64(self) -> np.ndarray:

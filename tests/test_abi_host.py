@@ -32,7 +32,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("store_kvcache", "paged_attn_decode", "paged_attn_prefill_varlen",
+    for n in ("store_kvcache", "paged_attn_decode", "paged_attn_decode_store",
+              "paged_attn_prefill_varlen",
               "paged_attn_decode_workspace_bytes", "pkv_prefill_metadata", "pkv_decode_metadata",
               "pkv_status_string"):
         assert n in names
@@ -122,6 +123,29 @@ def _decode_rc(**kw):
                                               a["W"], a["ctx"], a["B"], a["Hq"], a["Hkv"], a["D"],
                                               a["bs"], a["scale"], a["dt"], a["part"], a["ws"],
                                               a["ws_bytes"], None)
+
+
+def _decode_store_rc(**kw):
+    a = dict(out=FAKE, q=FAKE, key=FAKE, ks=1024, value=FAKE, vs=1024, slots=FAKE, k=FAKE, v=FAKE,
+             nb=16, bt=FAKE, W=4, ctx=FAKE, B=2, Hq=16, Hkv=8, D=128, bs=256, scale=0.1,
+             dt=B.PKV_BF16, part=0, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return B.load_library().paged_attn_decode_store(
+        a["out"], a["q"], a["key"], a["ks"], a["value"], a["vs"], a["slots"], a["k"], a["v"],
+        a["nb"], a["bt"], a["W"], a["ctx"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+        a["scale"], a["dt"], a["part"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(key=None), -1), (dict(value=None), -1), (dict(slots=None), -1),
+    (dict(ks=1000), -1), (dict(vs=1020), -1),             # token stride below Hkv * D
+    (dict(ks=1028), -1),                                  # 2056-byte stride: not 16-byte rows
+    (dict(key=ctypes.c_void_p(0x1004)), -1), (dict(value=ctypes.c_void_p(0x1008)), -1),
+    (dict(dt=7), -2), (dict(D=96), -2), (dict(ws_bytes=16), -3), (dict(B=0), 0),
+    (dict(B=0, key=None), 0),
+])
+def test_decode_store_argument_validation(kw, status):
+    assert _decode_store_rc(**kw) == status
 
 
 def _prefill_rc(**kw):
