@@ -376,9 +376,10 @@ __device__ __forceinline__ void bits_to_float(const typename LaneBits<T, DPL>::t
 // wavefront per (sequence, head), four per workgroup. The kernel is latency bound, so it
 // takes two rounds of loads: first the split metadata together with the (m, l) of the
 // first 64 slots (lane p holds slot p; the slots exist for every row, so they are read
-// before the row's slot count is known) and, for the fused store, q and the newest token's
-// rows; then the o rows of up to 16 slots at a time, D / 64 consecutive floats per lane
-// (one coalesced row per load instruction).
+// before the row's slot count is known), the o rows of the first kSpec slots and, for the
+// fused store, q and the newest token's rows; then the o rows of the remaining slots, up
+// to 16 at a time, D / 64 consecutive floats per lane (one coalesced row per load
+// instruction). A row cut into at most kSpec pieces needs no second round.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     T* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t cap,
@@ -387,6 +388,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     const int32_t* __restrict__ ws_meta, int32_t per_seq_line, NewTokens nt) {
   constexpr int DPL = D / 64;  // floats per lane
   constexpr int OB = 16;       // o rows per load batch
+  constexpr int kSpec = 4;     // o rows loaded in the first round, before the count is known
   static_assert(DPL == 1 || DPL == 2, "head_dim 64 or 128");
   typedef typename LaneBits<T, DPL>::type Bits;
   const int lane = threadIdx.x & 63;
@@ -404,6 +406,18 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   if (lane < max_pieces) {
     mp = ws_ml[2 * (base + lane)];
     lp = ws_ml[2 * (base + lane) + 1];
+  }
+  float ov0[kSpec][DPL];
+#pragma unroll
+  for (int u = 0; u < kSpec; ++u) {
+    const float* src = ws_o + (base + min(u, max_pieces - 1)) * D + lane * DPL;
+    if constexpr (DPL == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(src);
+      ov0[u][0] = v.x;
+      ov0[u][1] = v.y;
+    } else {
+      ov0[u][0] = *src;
+    }
   }
   Bits qw{}, kw{}, vw{};
   int slot = -1;
@@ -447,12 +461,18 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[e] *= rescale;
       M = Mn;
-      // round 2: the o rows
+      // round 2: the o rows not loaded yet
       for (int p = 0; p < cnt; p += OB) {
         float ov[OB][DPL];
 #pragma unroll
         for (int u = 0; u < OB; ++u) {
-          const float* src = ws_o + (base + p0 + min(p + u, cnt - 1)) * D + lane * DPL;
+          if (u < kSpec && p0 == 0 && p == 0) {
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) ov[u][e] = ov0[u < kSpec ? u : 0][e];
+            continue;
+          }
+          if (p + u >= cnt) continue;
+          const float* src = ws_o + (base + p0 + p + u) * D + lane * DPL;
           if constexpr (DPL == 2) {
             const float2 v = *reinterpret_cast<const float2*>(src);
             ov[u][0] = v.x;
