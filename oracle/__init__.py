@@ -16,4 +16,5 @@ from .paged_attention import (  # noqa: F401
     softmax_probs,
     paged_attn_decode,
     paged_attn_prefill_varlen,
+    attn_prefill_varlen,
 )

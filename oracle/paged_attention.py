@@ -23,7 +23,8 @@ Every function is the plain definition of what the path computes:
 Readings where the pages are silent (each is listed with its support in the
 design notes): GQA maps q head h to kv head h // (Hq / Hkv); a decode row with
 context length 0 yields zeros; duplicate non-negative slots in one store are
-rejected; prefill always reads K/V through the block table.
+rejected; the paged prefill always reads K/V through the block table, and the packed
+form (no block table) takes sequence b's keys from rows cu_k[b]..cu_k[b+1]-1.
 
 Pins: tests/test_oracle_pins.py checks every function here against the pages'
 worked example, pure-Python brute force, closed forms, torch's fp64 SDPA and
@@ -231,6 +232,32 @@ def paged_attn_decode(q, k_cache, v_cache, dtype, block_tables, context_lens, sc
         K = gather_kv(k_cache, dtype, block_tables[b], n, block_size)
         V = gather_kv(v_cache, dtype, block_tables[b], n, block_size)
         out[b] = attend(q[b:b + 1], K, V, [n - 1], scale)[0]
+    return out
+
+
+def attn_prefill_varlen(q, k, v, dtype, cu_seqlens_q, cu_seqlens_k, scale, seqs=None) -> np.ndarray:
+    """Causal varlen prefill over packed K/V rows, no block table ([P1] Attention.forward,
+    prefill branch when the context carries no block tables: the step's own k and v).
+
+    Sequence b owns query rows ``cu_q[b]..cu_q[b+1]-1`` and key/value rows
+    ``cu_k[b]..cu_k[b+1]-1`` of ``k`` / ``v`` ([total_k, Hkv, D]); with ``Lq`` queries and
+    ``Lk`` keys, query i sits at position ``Lk - Lq + i`` as in the paged form.
+    """
+    q = to_f64(q, dtype)
+    T, Hq, D = q.shape
+    out = np.zeros((T, Hq, D))
+    B = len(cu_seqlens_q) - 1
+    for b in (range(B) if seqs is None else seqs):
+        q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+        k0, k1 = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])
+        Lq, Lk = q1 - q0, k1 - k0
+        if Lq == 0:
+            continue
+        if Lk < Lq:
+            raise ValueError("a sequence has fewer keys than queries")
+        K = to_f64(k[k0:k1], dtype)
+        V = to_f64(v[k0:k1], dtype)
+        out[q0:q1] = attend(q[q0:q1], K, V, Lk - Lq + np.arange(Lq), scale)
     return out
 
 

@@ -138,6 +138,33 @@ def test_oracle_matches_brute_force(idx):
     assert np.max(np.abs(out - ref)) <= 1e-12
 
 
+def packed_kv(w):
+    """The workload's logical K/V rows packed sequence after sequence, and cu_seqlens_k."""
+    ks, vs = zip(*(w.seq_kv_logical(b) for b in range(w.num_seqs)))
+    cu_k = np.concatenate([[0], np.cumsum(w.seq_lens)]).astype(np.int64)
+    return np.concatenate(ks), np.concatenate(vs), cu_k
+
+
+@pytest.mark.parametrize("idx", [3, 4, 5])
+def test_packed_prefill_matches_brute_force(idx):
+    w = tiny_workloads()[idx]
+    k, v, cu_k = packed_kv(w)
+    cu_q = np.concatenate([[0], np.cumsum(w.q_lens)]).astype(np.int64)
+    out = O.attn_prefill_varlen(w.q, k, v, w.dtype, cu_q, cu_k, w.scale)
+    ref = brute_force(w)
+    assert out.shape == ref.shape
+    assert np.max(np.abs(out - ref)) <= 1e-12
+
+
+def test_packed_prefill_equals_paged_prefill():
+    w = make_prefill(22, [5, 0, 9, 3], cached=[8, 3, 0, 13], Hq=4, Hkv=2, D=8, dtype="bf16",
+                     bs=4, shared_blocks=[2, 0, 0, 2], n_prefix_blocks=2)
+    out, md, _, _ = run_workload(w)
+    k, v, cu_k = packed_kv(w)
+    packed = O.attn_prefill_varlen(w.q, k, v, w.dtype, md["cu_seqlens_q"], cu_k, w.scale)
+    np.testing.assert_array_equal(out, packed)
+
+
 # ---------------------------------------------------------------- closed forms
 def test_single_key_returns_that_value_row():
     w = make_decode(11, [1, 1, 1], Hq=4, Hkv=2, D=16, dtype="bf16", bs=8)
