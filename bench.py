@@ -160,6 +160,31 @@ def bench_prefill(torch, cfg, iters, warmup):
             "store_us_median": st_med * 1e3, "store_gbs": store_bytes(w) / (st_med * 1e-3) / 1e9}
 
 
+def bench_prefill_packed(torch, iters, warmup):
+    """The varlen workload through attn_prefill_varlen: the step's own K/V rows, packed,
+    no block table (the engine's path when no prefix is cached)."""
+    from paged_kv_cache_225_amd import _binding as B
+    from paged_kv_cache_225_amd.harness import DeviceStep
+    from workloads import CONFIG_NAMES, make_config
+    w = make_config(3)
+    assert int(w.num_cached.sum()) == 0
+    ds = DeviceStep(w)
+    stream = torch.cuda.current_stream()
+    mk = int(w.seq_lens.max())
+
+    def call():
+        B.attn_prefill_varlen(ds.out, ds.q, ds.new_k, ds.new_v, ds.cu_seqlens_q, ds.cu_seqlens_k,
+                              ds.max_seqlen_q, mk, w.scale, stream=stream)
+
+    med, p10, p90 = _median_event_ms(torch, call, iters, warmup, stream)
+    flops, _ = prefill_flops(w)
+    tf = flops / (med * 1e-3) / 1e12
+    return {"workload": CONFIG_NAMES[3] + "_packed_kv", "attn_us_median": med * 1e3,
+            "attn_us_p10_p90": [p10 * 1e3, p90 * 1e3], "flops": flops, "tflops": tf,
+            "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
+            "tokens_per_s": float(w.q_lens.sum()) / (med * 1e-3)}
+
+
 def bench_large_decode(torch, iters, warmup):
     from paged_kv_cache_225_amd.harness import DeviceStep
     from workloads import CONFIG_NAMES, make_config
@@ -257,7 +282,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
                     help="copy: run a plain 1 GiB device copy (HBM counter calibration)")
-    ap.add_argument("--only", choices=["prefill3", "prefill4", "large"], default=None,
+    ap.add_argument("--only", choices=["prefill3", "prefill4", "prefill3packed", "large"], default=None,
                     help="run one secondary workload alone (for profiler passes)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -274,8 +299,12 @@ def main():
         copy_calibration(torch, args.steps)
         return
     if args.only is not None:
-        res = (bench_large_decode(torch, args.iters, 5) if args.only == "large"
-               else bench_prefill(torch, 3 if args.only == "prefill3" else 4, args.iters, 5))
+        if args.only == "large":
+            res = bench_large_decode(torch, args.iters, 5)
+        elif args.only == "prefill3packed":
+            res = bench_prefill_packed(torch, args.iters, 5)
+        else:
+            res = bench_prefill(torch, 3 if args.only == "prefill3" else 4, args.iters, 5)
         print(json.dumps({"only": args.only, **res}), flush=True)
         return
     print("bench: decode headline", file=sys.stderr, flush=True)
@@ -309,7 +338,8 @@ def main():
     }
     if not args.no_secondary:
         print("bench: prefill workloads", file=sys.stderr, flush=True)
-        line["prefill"] = [bench_prefill(torch, 3, args.iters, 5), bench_prefill(torch, 4, args.iters, 5)]
+        line["prefill"] = [bench_prefill(torch, 3, args.iters, 5), bench_prefill(torch, 4, args.iters, 5),
+                           bench_prefill_packed(torch, args.iters, 5)]
         print("bench: large decode workload", file=sys.stderr, flush=True)
         line["large_decode"] = bench_large_decode(torch, args.iters, 5)
     if not args.no_cpu_baseline:

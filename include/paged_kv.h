@@ -230,6 +230,40 @@ int paged_attn_prefill_varlen(void* out, const void* q,
                               int32_t block_size, float scale, int32_t causal,
                               pkv_dtype_t dtype, hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------
+ * Varlen causal prefill over packed K/V - [P1] Attention.forward, prefill branch when the
+ * context holds no block tables (no prefix-cache hit): flash_attn_varlen_func on the step's
+ * own k and v instead of the caches.
+ * Same operation as paged_attn_prefill_varlen, except that sequence b's keys are rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k and v (Lk of them) rather than positions read
+ * through a block table.
+ *   out, q       device [total_q, Hq, D] bf16, contiguous (packed sequences)
+ *   k, v         device [rows, Hkv, D] bf16 with token strides *_token_stride elements
+ *                (>= Hkv * D, multiples of 8, so every row starts on 16 bytes; head stride D,
+ *                unit element stride - a view into a fused qkv buffer works)
+ *   cu_seqlens_q, cu_seqlens_k  device int32 [num_seqs + 1]
+ *   max_seqlen_q, max_seqlen_k  host ints: upper bounds of every Lq and every Lk; max_seqlen_k
+ *                sizes the launch (one plane of workgroups per possible count of 64-key tiles)
+ *   causal       must be 1.
+ * out, q, k and v must be 16-byte aligned (PKV_ERR_INVALID otherwise).
+ * Preconditions: cu_seqlens_q[num_seqs] == total_q; Lq <= max_seqlen_q; Lk >= Lq;
+ * Lk <= max_seqlen_k (a sequence breaking this may have rows left unwritten); the rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 exist in k and v.
+ * Supported: bf16 only (fp32 accumulation); D in {64, 128}; G in {1, 2, 4, 8};
+ * num_seqs <= 65535; ceil(max_seqlen_k / 64) <= 65535; token strides < 2^31 / 64.
+ * Errors: PKV_ERR_INVALID (also max_seqlen_k < max_seqlen_q, bad strides or alignment),
+ * PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.
+ * -------------------------------------------------------------------------------------*/
+int attn_prefill_varlen(void* out, const void* q,
+                        const void* k, int64_t k_token_stride,
+                        const void* v, int64_t v_token_stride,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        int32_t num_seqs, int32_t total_q,
+                        int32_t max_seqlen_q, int32_t max_seqlen_k,
+                        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                        float scale, int32_t causal, pkv_dtype_t dtype,
+                        hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

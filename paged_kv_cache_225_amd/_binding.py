@@ -38,6 +38,8 @@ SIGNATURES = {
     "paged_attn_decode_store": (_c_int, [_p, _p, _p, _i64, _p, _i64, _p, _p, _p, _i32, _p, _i32,
                                          _p, _i32, _i32, _i32, _i32, _i32, _f, _c_int, _i32, _p,
                                          _size, _p]),
+    "attn_prefill_varlen": (_c_int, [_p, _p, _p, _i64, _p, _i64, _p, _p, _i32, _i32, _i32, _i32,
+                                     _i32, _i32, _i32, _f, _i32, _c_int, _p]),
     "paged_attn_prefill_varlen": (_c_int, [_p, _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32,
                                            _i32, _i32, _i32, _i32, _i32, _i32, _f, _i32, _c_int,
                                            _p]),
@@ -229,3 +231,20 @@ def paged_attn_prefill_varlen(out, q, k_cache, v_cache, block_tables, cu_seqlens
         W, _t_ptr(cu_seqlens_q), _t_ptr(cu_seqlens_k), B, T, int(max_seqlen_q), int(max_seqlen_k),
         Hq, Hkv, D, bs, float(scale), 1 if causal else 0, _dtype_code(q), _stream(stream))
     _check("paged_attn_prefill_varlen", rc)
+
+
+def attn_prefill_varlen(out, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                        scale, causal=True, stream=None):
+    """out/q [total_q, Hq, D] bf16; k/v [rows, Hkv, D] bf16 packed key/value rows (token
+    stride free, head stride D, unit element stride); cu_seqlens_q/k int32 [B+1] on the
+    device; max_seqlen_q/k host ints."""
+    T, Hq, D = q.shape
+    _, Hkv, _ = k.shape
+    if k.stride(2) != 1 or k.stride(1) != D or v.stride(2) != 1 or v.stride(1) != D:
+        raise ValueError("k/v need head stride head_dim and unit element stride")
+    B = cu_seqlens_q.numel() - 1
+    rc = load_library().attn_prefill_varlen(
+        _t_ptr(out), _t_ptr(q), _t_ptr(k), k.stride(0), _t_ptr(v), v.stride(0),
+        _t_ptr(cu_seqlens_q), _t_ptr(cu_seqlens_k), B, T, int(max_seqlen_q), int(max_seqlen_k),
+        Hq, Hkv, D, float(scale), 1 if causal else 0, _dtype_code(q), _stream(stream))
+    _check("attn_prefill_varlen", rc)

@@ -290,6 +290,70 @@ int paged_attn_decode_store(void* out, const void* q, const void* key, int64_t k
 }
 
 // ------------------------------------------------------------------------- prefill
+}  // extern "C"
+
+namespace {
+
+// The shared body of paged_attn_prefill_varlen and attn_prefill_varlen (packed: the latter;
+// k / v then hold packed rows with the given token strides and no table is read).
+int prefill_common(void* out, const void* q, const void* k, const void* v, int32_t num_blocks,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                   int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                   int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, float scale, int32_t causal, pkv_dtype_t dtype,
+                   bool packed, int64_t k_stride, int64_t v_stride, hipStream_t stream) {
+  if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (causal != 1) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0) return PKV_ERR_INVALID;
+  if (!packed && (num_blocks < 0 || max_blocks_per_seq <= 0)) return PKV_ERR_INVALID;
+  if (max_seqlen_k < max_seqlen_q) return PKV_ERR_INVALID;  // every Lk >= its Lq
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return PKV_ERR_INVALID;
+  if (!packed && !pow2_at_least_16(block_size)) return PKV_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (!supported_group(num_heads, num_kv_heads)) return PKV_ERR_UNSUPPORTED;
+  if (!packed && (int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PKV_ERR_INVALID;
+  if (packed) {
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (k_stride < row || v_stride < row || k_stride % 8 || v_stride % 8) return PKV_ERR_INVALID;
+    if (k_stride > INT32_MAX / 64 || v_stride > INT32_MAX / 64) return PKV_ERR_UNSUPPORTED;
+  }
+  // the launch has one plane per possible count of 64-key tiles of a unit
+  const int64_t key_cap = packed ? INT32_MAX : (int64_t)max_blocks_per_seq * block_size;
+  const int64_t key_tiles = ((max_seqlen_k < key_cap ? max_seqlen_k : key_cap) + 63) / 64;
+  if (num_seqs > 65535 || key_tiles > 65535) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PKV_OK;
+  if (!out || !q || !k || !v || !cu_seqlens_q || !cu_seqlens_k) return PKV_ERR_INVALID;
+  if (!packed && !block_tables) return PKV_ERR_INVALID;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v)) return PKV_ERR_INVALID;
+  pkv::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k;
+  a.v_cache = v;
+  a.num_blocks = packed ? 0 : num_blocks;
+  a.block_tables = packed ? nullptr : block_tables;
+  a.max_blocks_per_seq = packed ? 0 : max_blocks_per_seq;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.cu_seqlens_k = cu_seqlens_k;
+  a.num_seqs = num_seqs;
+  a.key_tiles = (int32_t)key_tiles;
+  a.packed = packed ? 1 : 0;
+  a.k_stride = k_stride;
+  a.v_stride = v_stride;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = packed ? 0 : block_size;
+  a.scale = scale;
+  const int rc = pkv::launch_prefill(a, stream);
+  return rc == 0 ? PKV_OK : (rc == -2 ? PKV_ERR_UNSUPPORTED : PKV_ERR_HIP);
+}
+
+}  // namespace
+
+extern "C" {
+
 int paged_attn_prefill_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
                               int32_t num_blocks, const int32_t* block_tables,
                               int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
@@ -298,44 +362,21 @@ int paged_attn_prefill_varlen(void* out, const void* q, const void* k_cache, con
                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                               float scale, int32_t causal, pkv_dtype_t dtype,
                               hipStream_t stream) {
-  if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
-  if (causal != 1) return PKV_ERR_UNSUPPORTED;
-  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || num_blocks < 0 || max_blocks_per_seq <= 0)
-    return PKV_ERR_INVALID;
-  if (max_seqlen_k < max_seqlen_q) return PKV_ERR_INVALID;  // every Lk >= its Lq
-  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return PKV_ERR_INVALID;
-  if (!pow2_at_least_16(block_size)) return PKV_ERR_UNSUPPORTED;
-  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
-  if (!supported_group(num_heads, num_kv_heads)) return PKV_ERR_UNSUPPORTED;
-  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PKV_ERR_INVALID;
-  // the launch has one plane per possible count of 64-key tiles of a unit
-  const int64_t key_cap = (int64_t)max_blocks_per_seq * block_size;
-  const int64_t key_tiles = ((max_seqlen_k < key_cap ? max_seqlen_k : key_cap) + 63) / 64;
-  if (num_seqs > 65535 || key_tiles > 65535) return PKV_ERR_UNSUPPORTED;
-  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PKV_OK;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens_q || !cu_seqlens_k)
-    return PKV_ERR_INVALID;
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-    return PKV_ERR_INVALID;
-  pkv::PrefillArgs a;
-  a.out = out;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.num_blocks = num_blocks;
-  a.block_tables = block_tables;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.cu_seqlens_q = cu_seqlens_q;
-  a.cu_seqlens_k = cu_seqlens_k;
-  a.num_seqs = num_seqs;
-  a.key_tiles = (int32_t)key_tiles;
-  a.num_heads = num_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.block_size = block_size;
-  a.scale = scale;
-  const int rc = pkv::launch_prefill(a, stream);
-  return rc == 0 ? PKV_OK : (rc == -2 ? PKV_ERR_UNSUPPORTED : PKV_ERR_HIP);
+  return prefill_common(out, q, k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq,
+                        cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, max_seqlen_q,
+                        max_seqlen_k, num_heads, num_kv_heads, head_dim, block_size, scale,
+                        causal, dtype, false, 0, 0, stream);
+}
+
+int attn_prefill_varlen(void* out, const void* q, const void* k, int64_t k_token_stride,
+                        const void* v, int64_t v_token_stride, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t total_q,
+                        int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
+                        pkv_dtype_t dtype, hipStream_t stream) {
+  return prefill_common(out, q, k, v, 0, nullptr, 0, cu_seqlens_q, cu_seqlens_k, num_seqs,
+                        total_q, max_seqlen_q, max_seqlen_k, num_heads, num_kv_heads, head_dim,
+                        0, scale, causal, dtype, true, k_token_stride, v_token_stride, stream);
 }
 
 }  // extern "C"

@@ -70,6 +70,8 @@ struct PrefillArgs {
   const int32_t* cu_seqlens_k;
   int32_t num_seqs;
   int32_t key_tiles;         // grid planes: ceil(min(max_seqlen_k, table capacity) / 64)
+  int32_t packed;            // 1: k_cache / v_cache are packed K / V rows, no block table
+  int64_t k_stride, v_stride;  // packed: token strides in elements
   int32_t num_heads, num_kv_heads, head_dim, block_size;
   float scale;
 };

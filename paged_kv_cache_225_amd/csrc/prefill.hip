@@ -69,13 +69,17 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
 }
 
 // BIG_BLOCKS: blocks hold >= 64 keys, so every 64-key tile lies inside one block.
-template <int D, int GH, bool BIG_BLOCKS>
+// PACKED: no block table; sequence b's keys are rows cu_k[b] .. cu_k[b+1]-1 of k / v, with
+// token strides k_stride / v_stride (elements). The paged form passes Hkv * D for both.
+template <int D, int GH, bool BIG_BLOCKS, bool PACKED>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(
     __bf16* __restrict__ out, const __bf16* __restrict__ q, const __bf16* __restrict__ k_cache,
     const __bf16* __restrict__ v_cache, int32_t num_blocks,
     const int32_t* __restrict__ block_tables, int32_t bt_stride,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_heads,
-    int32_t num_kv_heads, int32_t bs_log2, float scale_log2e) {
+    int32_t num_kv_heads, int32_t bs_log2, float scale_log2e, int64_t k_stride,
+    int64_t v_stride) {
+  static_assert(BIG_BLOCKS || !PACKED, "packed rows take the one-base-per-tile path");
   constexpr int KS = D / 32;                 // k-steps of the QK^T product
   constexpr int DT = D / 16;                 // 16-row tiles of O^T
   constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     const int Lq = cu_q[b + 1] - q_begin;
     const int cap = bt_stride << bs_log2;
     int Lk = cu_k[b + 1] - cu_k[b];
-    Lk = Lk > cap ? cap : Lk;
+    if constexpr (!PACKED) Lk = Lk > cap ? cap : Lk;
     const int t = (Lk + kBK - 1) / kBK - ((int)gridDim.z - z);
     if (t < 0) return;              // no unit of this length in this sequence
     const int i_hi = Lq - kBQ * t;  // exclusive end of this unit's query rows
@@ -123,7 +127,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     const int wave_min_pos = off + i_lo + wave * 16;
 
     const int64_t row_elems = (int64_t)num_kv_heads * D;
-    const int32_t* bt = block_tables + (int64_t)b * bt_stride;
+    const int32_t* bt = PACKED ? nullptr : block_tables + (int64_t)b * bt_stride;
+    const int64_t k_row0 = PACKED ? cu_k[b] : 0;  // packed: the sequence's first key row
     const int bs_mask = (1 << bs_log2) - 1;
 
     // Q^T operands: lane holds 8 dims of its query column for each k-step
@@ -157,11 +162,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     int lane_off_k[NL], lane_off_v[NL];  // elements from the tile's first row
   #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      lane_off_k[i] = lrow[i] * (int)row_elems + g * D + 8 * kchunk[i];
-      lane_off_v[i] = lrow[i] * (int)row_elems + g * D + 8 * vchunk[i];
+      lane_off_k[i] = lrow[i] * (int)k_stride + g * D + 8 * kchunk[i];
+      lane_off_v[i] = lrow[i] * (int)v_stride + g * D + 8 * vchunk[i];
     }
     int nblk[NL];  // block ids of this lane's rows for a tile two steps ahead
     auto fetch_blocks = [&](int kt) {
+      if constexpr (PACKED) return;
       if constexpr (BIG_BLOCKS) {  // one id, the same for every lane (nblk[1..] unused)
         nblk[0] = kt < n_kt ? bt[(kt * kBK) >> bs_log2] : -1;
         return;
@@ -174,12 +180,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     };
     auto issue_tile = [&](int kt, char (*dst)[TILEB], const int* blk) {
       if constexpr (BIG_BLOCKS) {
-        const int b0 = __builtin_amdgcn_readfirstlane(blk[0]);
-        const bool blk_ok = (unsigned)b0 < (unsigned)num_blocks;
-        const int64_t base =
-            blk_ok ? ((int64_t)b0 << bs_log2 | ((kt * kBK) & bs_mask)) * row_elems : 0;
-        const __bf16* kb = k_cache + base;
-        const __bf16* vb = v_cache + base;
+        bool blk_ok = true;
+        int64_t base_k, base_v;
+        if constexpr (PACKED) {
+          base_k = (k_row0 + kt * kBK) * k_stride;
+          base_v = (k_row0 + kt * kBK) * v_stride;
+        } else {
+          const int b0 = __builtin_amdgcn_readfirstlane(blk[0]);
+          blk_ok = (unsigned)b0 < (unsigned)num_blocks;
+          base_k = blk_ok ? ((int64_t)b0 << bs_log2 | ((kt * kBK) & bs_mask)) * row_elems : 0;
+          base_v = base_k;
+        }
+        const __bf16* kb = k_cache + base_k;
+        const __bf16* vb = v_cache + base_v;
         if (blk_ok && (kt + 1) * kBK <= Lk) {  // a full tile of real keys: loads only
   #pragma unroll
           for (int i = 0; i < NL; ++i) {
@@ -417,20 +430,23 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   unit(blockIdx.x, b, z);
 }
 
-template <int D, int GH, bool BIG_BLOCKS>
+template <int D, int GH, bool BIG_BLOCKS, bool PACKED = false>
 static int run_prefill(const PrefillArgs& a, hipStream_t stream) {
-  const int bs_log2 = __builtin_ctz((unsigned)a.block_size);
+  const int bs_log2 = PACKED ? 0 : __builtin_ctz((unsigned)a.block_size);
+  const int64_t row = (int64_t)a.num_kv_heads * D;
   dim3 grid(a.num_heads / GH, a.num_seqs, a.key_tiles);
-  hipLaunchKernelGGL((prefill_kernel<D, GH, BIG_BLOCKS>), grid, dim3(256), 0, stream,
+  hipLaunchKernelGGL((prefill_kernel<D, GH, BIG_BLOCKS, PACKED>), grid, dim3(256), 0, stream,
                      (__bf16*)a.out, (const __bf16*)a.q, (const __bf16*)a.k_cache,
                      (const __bf16*)a.v_cache, a.num_blocks, a.block_tables,
                      a.max_blocks_per_seq, a.cu_seqlens_q, a.cu_seqlens_k, a.num_heads,
-                     a.num_kv_heads, bs_log2, a.scale * kLog2e);
+                     a.num_kv_heads, bs_log2, a.scale * kLog2e, PACKED ? a.k_stride : row,
+                     PACKED ? a.v_stride : row);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 template <int D, int GH>
 static int run_prefill_bs(const PrefillArgs& a, hipStream_t stream) {
+  if (a.packed) return run_prefill<D, GH, true, true>(a, stream);
   return a.block_size >= kBK ? run_prefill<D, GH, true>(a, stream) : run_prefill<D, GH, false>(a, stream);
 }
 

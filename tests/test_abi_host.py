@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("store_kvcache", "paged_attn_decode", "paged_attn_decode_store",
-              "paged_attn_prefill_varlen",
+              "paged_attn_prefill_varlen", "attn_prefill_varlen",
               "paged_attn_decode_workspace_bytes", "pkv_prefill_metadata", "pkv_decode_metadata",
               "pkv_status_string"):
         assert n in names
@@ -202,3 +202,24 @@ def test_workspace_query():
     assert B.paged_attn_decode_workspace_bytes(4, 16, 128, 16, 256, 256) == expect(4, 16, 128, 16, 256, 256)
     assert B.paged_attn_decode_workspace_bytes(4, 16, 128, 16, 256, 0) == expect(4, 16, 128, 16, 256, 256)
     assert B.paged_attn_decode_workspace_bytes(4, 16, 128, 16, 256, 100) == 0     # invalid partition
+
+
+def _packed_rc(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, ks=1024, v=FAKE, vs=1024, cq=FAKE, ck=FAKE, B=2, T=10,
+             mq=8, mk=8, Hq=16, Hkv=8, D=128, scale=0.1, causal=1, dt=B.PKV_BF16)
+    a.update(kw)
+    return B.load_library().attn_prefill_varlen(
+        a["out"], a["q"], a["k"], a["ks"], a["v"], a["vs"], a["cq"], a["ck"], a["B"], a["T"],
+        a["mq"], a["mk"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=B.PKV_F32), -2), (dict(causal=0), -2), (dict(D=80), -2), (dict(Hq=12, Hkv=4), -2),
+    (dict(q=None), -1), (dict(k=None), -1), (dict(cq=None), -1),
+    (dict(ks=1000), -1), (dict(vs=1020), -1), (dict(ks=1028), -1),   # short or not 16-byte rows
+    (dict(k=ctypes.c_void_p(0x1004)), -1), (dict(v=ctypes.c_void_p(0x1008)), -1),
+    (dict(out=ctypes.c_void_p(0x1002)), -1),
+    (dict(mk=7), -1), (dict(mk=1 << 23), -2), (dict(B=0), 0), (dict(T=0), 0), (dict(mq=0), 0),
+])
+def test_packed_prefill_argument_validation(kw, status):
+    assert _packed_rc(**kw) == status
