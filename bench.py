@@ -9,9 +9,10 @@ beside it. Consecutive steps rotate over several layer pools (each a full copy o
 2048-block K/V pool, as every layer of the engine owns its own cache), so the KV read
 streams from HBM rather than from the 256 MB last-level cache.
 
-The same JSON line also carries the prefill half of the metric (the varlen prefill and
-the prefix-cached prefill workloads, in TFLOP/s against the bf16 MFMA peak), the large
-decode workload (512 sequences, shared prefixes) and the host metadata time.
+The same JSON line also carries the prefill half of the metric (the varlen prefill, the
+prefix-cached prefill and the chunked prefill workloads, in TFLOP/s against the bf16 MFMA
+peak), the large decode workload (512 sequences, shared prefixes), small-batch decode steps
+replayed from recorded graphs next to eager calls, and the host metadata time.
 
 ``value`` is the decode step's algorithmic bytes per second (KV rows of every visible key
 once per sequence and kv head, plus q, out, tables, and the store's reads and writes).
@@ -144,9 +145,14 @@ def bench_decode_headline(torch, args):
 
 
 def bench_prefill(torch, cfg, iters, warmup):
+    """Prefill workload `cfg` (3: varlen, 4: prefix-cached, "chunked": chunked prefill with
+    unaligned resident prefixes): the step's store, then attention through the tables."""
     from paged_kv_cache_225_amd.harness import DeviceStep
-    from workloads import CONFIG_NAMES, make_config
-    w = make_config(cfg)
+    from workloads import CHUNKED_PREFILL_NAME, CONFIG_NAMES, make_chunked_prefill, make_config
+    if cfg == "chunked":
+        w, name = make_chunked_prefill(), CHUNKED_PREFILL_NAME
+    else:
+        w, name = make_config(cfg), CONFIG_NAMES[cfg]
     ds = DeviceStep(w)
     stream = torch.cuda.current_stream()
     ds.store(stream)
@@ -154,7 +160,7 @@ def bench_prefill(torch, cfg, iters, warmup):
     st_med, _, _ = _median_event_ms(torch, lambda: ds.store(stream), iters, warmup, stream)
     flops, pairs = prefill_flops(w)
     tf = flops / (med * 1e-3) / 1e12
-    return {"workload": CONFIG_NAMES[cfg], "attn_us_median": med * 1e3, "attn_us_p10_p90": [p10 * 1e3, p90 * 1e3],
+    return {"workload": name, "attn_us_median": med * 1e3, "attn_us_p10_p90": [p10 * 1e3, p90 * 1e3],
             "flops": flops, "tflops": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
             "tokens_per_s": float(w.q_lens.sum()) / (med * 1e-3),
             "store_us_median": st_med * 1e3, "store_gbs": store_bytes(w) / (st_med * 1e-3) / 1e9}
@@ -200,6 +206,51 @@ def bench_large_decode(torch, iters, warmup):
             "unique_gbs": uniq / (med * 1e-3) / 1e9, "logical_gbs": logi / (med * 1e-3) / 1e9,
             "frac_hbm_unique": uniq / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "tokens_per_s": w.num_seqs / (med * 1e-3), "shared_hist": w.meta.get("shared_hist")}
+
+
+def bench_graph_decode(torch, iters):
+    """Decode steps of small batches replayed from the library's recorded graphs (one graph
+    launch per step) next to the same call made eagerly (one library call, two kernel
+    launches). Both loops issue `iters` back-to-back steps between two synchronisations;
+    the rows are a seeded subset of the batch-64 workload's sequences."""
+    from paged_kv_cache_225_amd import _binding as B
+    from paged_kv_cache_225_amd.harness import DeviceStep, GraphDecodeStep
+    from workloads import make_config
+    w = make_config(2)
+    ds = DeviceStep(w)
+    gs = GraphDecodeStep(ds, 64, width=16)
+    stream = torch.cuda.current_stream()
+    rng = np.random.Generator(np.random.PCG64(77))
+    rows = []
+    for b in (1, 4, 16, 64):
+        seqs = rng.choice(w.num_seqs, size=b, replace=False)
+        gs.load(seqs)
+        n = gs.graphs.bucket(b)
+
+        def eager():
+            B.paged_attn_decode_store(gs.out[:b], gs.q[:b], gs.key[:b], gs.value[:b],
+                                      gs.slots[:b], ds.k_cache, ds.v_cache, gs.tables[:b],
+                                      gs.ctx[:b], w.scale, workspace=gs.workspace, stream=stream)
+
+        def graph():
+            gs.launch(b, stream)
+
+        res = {"batch": b, "bucket": n}
+        for name, fn in (("eager", eager), ("graph", graph)):
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(iters):
+                fn()
+            torch.cuda.synchronize()
+            res[name + "_us_per_step"] = (time.perf_counter() - t0) / iters * 1e6
+        rows.append(res)
+    return {"workload": "decode steps of 1/4/16/64 sequences from the batch-64 workload "
+                        "(ctx U[256,4096], 16q/8kv heads, d128, bf16)",
+            "note": "wall time per step over back-to-back steps, both legs on the same "
+                    "buffers; a small batch's K/V stays in the last-level cache across steps",
+            "steps": rows}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b64_hbm_traffic.json")
@@ -282,7 +333,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
                     help="copy: run a plain 1 GiB device copy (HBM counter calibration)")
-    ap.add_argument("--only", choices=["prefill3", "prefill4", "prefill3packed", "large"], default=None,
+    ap.add_argument("--only", choices=["prefill3", "prefill4", "prefill3packed", "chunked", "large",
+                                       "graph"], default=None,
                     help="run one secondary workload alone (for profiler passes)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -303,6 +355,10 @@ def main():
             res = bench_large_decode(torch, args.iters, 5)
         elif args.only == "prefill3packed":
             res = bench_prefill_packed(torch, args.iters, 5)
+        elif args.only == "chunked":
+            res = bench_prefill(torch, "chunked", args.iters, 5)
+        elif args.only == "graph":
+            res = bench_graph_decode(torch, 200)
         else:
             res = bench_prefill(torch, 3 if args.only == "prefill3" else 4, args.iters, 5)
         print(json.dumps({"only": args.only, **res}), flush=True)
@@ -339,9 +395,12 @@ def main():
     if not args.no_secondary:
         print("bench: prefill workloads", file=sys.stderr, flush=True)
         line["prefill"] = [bench_prefill(torch, 3, args.iters, 5), bench_prefill(torch, 4, args.iters, 5),
-                           bench_prefill_packed(torch, args.iters, 5)]
+                           bench_prefill_packed(torch, args.iters, 5),
+                           bench_prefill(torch, "chunked", args.iters, 5)]
         print("bench: large decode workload", file=sys.stderr, flush=True)
         line["large_decode"] = bench_large_decode(torch, args.iters, 5)
+        print("bench: graph-replayed small-batch decode", file=sys.stderr, flush=True)
+        line["graph_decode"] = bench_graph_decode(torch, 200)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

@@ -130,12 +130,15 @@ int store_kvcache(const void* key, int64_t key_token_stride,
  *                ceil(n / bs) are never read (padding -1 or stale ids are fine).
  *   context_lens device int32 [num_seqs]; 0 gives a zero output row without reading memory.
  *   partition_size  smallest share of keys per wavefront, a multiple of 64 in [64, 1024];
- *                0 = library default (256). It also sizes the workspace.
+ *                0 = library default: 64 keys when num_seqs * max_blocks_per_seq * bs
+ *                < 65536, 128 up to 131072, 256 above (a small batch then spreads over
+ *                more workgroups). It also sizes the workspace.
  *   workspace    device scratch of at least paged_attn_decode_workspace_bytes(...) bytes
  *                (same num_seqs, heads, head_dim, max_blocks_per_seq, block_size and
- *                partition_size), owned by the caller; no initial contents needed; in use
- *                until the stream passes the end of the call, so calls that overlap on
- *                different streams need different workspaces.
+ *                partition_size; with partition_size 0 the bytes for num_seqs also cover
+ *                every call with fewer sequences), owned by the caller; no initial
+ *                contents needed; in use until the stream passes the end of the call, so
+ *                calls that overlap on different streams need different workspaces.
  * out, q, k_cache, v_cache and workspace must be 16-byte aligned (PKV_ERR_INVALID otherwise).
  * Preconditions: num_blocks >= 1; n <= max_blocks_per_seq * bs (larger n is clamped to
  * that); table entries below ceil(n / bs) lie in [0, num_blocks) - an entry outside it is
@@ -188,6 +191,54 @@ int paged_attn_decode_store(void* out, const void* q,
                             int32_t block_size, float scale, pkv_dtype_t dtype,
                             int32_t partition_size, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Decode steps replayed from captured HIP graphs - [P1] ModelRunner.capture_cudagraph and
+ * run_model; [P2] cuda graph捕捉与context设置 (why: a recorded graph fixes shapes and device
+ * addresses, and one graph launch replaces the step's kernel launches).
+ *
+ * pkv_decode_graphs_create records one paged_attn_decode_store call per batch bucket
+ * (1, 2, 4, 8, then every multiple of 16 up to max_batch, plus max_batch itself when it is
+ * not a multiple of 16) over caller-owned static buffers sized for max_batch rows:
+ *   out, q       device [max_batch, Hq, D]; key, value device [max_batch, Hkv, D] with
+ *                token strides; slot_mapping, context_lens device int32 [max_batch];
+ *   block_tables device int32 [max_batch, max_blocks_per_seq];
+ *   workspace    device, >= paged_attn_decode_workspace_bytes(max_batch, ...) bytes.
+ * The other arguments are those of paged_attn_decode_store. Recording launches nothing.
+ * pkv_decode_graphs_launch(h, B, stream) replays, on `stream`, the graph of the smallest
+ * bucket >= B: it computes rows 0 .. bucket-1 of the buffers as they hold at that point in
+ * the stream. As in [P1] run_model, the caller writes the step's B rows and pads rows
+ * B .. bucket-1 with context_lens 0 and slot_mapping -1 (they get zero rows and store
+ * nothing; their block-table rows are never read). Every data-dependent quantity is
+ * computed on the device at run time, so any lengths up to max_blocks_per_seq * bs work.
+ * Ownership: the handle owns the graphs only; the buffers stay the caller's and must
+ * outlive the handle. One replay at a time per handle (replays share the workspace).
+ * pkv_decode_graphs_bucket(h, B) returns that bucket (or a negative status);
+ * pkv_decode_graphs_count / _buckets report the bucket list (ascending).
+ * Errors: PKV_ERR_INVALID (null handle, max_batch outside 1 .. 16383, B outside
+ * 1 .. max_batch), PKV_ERR_WORKSPACE, any status paged_attn_decode_store returns for the
+ * recorded call, PKV_ERR_HIP (capture, instantiation or launch failed). On error, create
+ * leaves *handle NULL and frees what it made.
+ * -------------------------------------------------------------------------------------*/
+typedef struct pkv_decode_graphs pkv_decode_graphs;
+
+int pkv_decode_graphs_create(pkv_decode_graphs** handle, int32_t max_batch,
+                             void* out, const void* q,
+                             const void* key, int64_t key_token_stride,
+                             const void* value, int64_t value_token_stride,
+                             const int32_t* slot_mapping,
+                             void* k_cache, void* v_cache, int32_t num_blocks,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens,
+                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, float scale, pkv_dtype_t dtype,
+                             int32_t partition_size, void* workspace, size_t workspace_bytes);
+int pkv_decode_graphs_count(const pkv_decode_graphs* handle);
+int pkv_decode_graphs_buckets(const pkv_decode_graphs* handle, int32_t* buckets,
+                              int32_t capacity);
+int pkv_decode_graphs_bucket(const pkv_decode_graphs* handle, int32_t batch);
+int pkv_decode_graphs_launch(pkv_decode_graphs* handle, int32_t batch, hipStream_t stream);
+int pkv_decode_graphs_destroy(pkv_decode_graphs* handle);
 
 /* ------------------------------------------------------------------------------------
  * Varlen causal prefill - [P1] Attention.forward (prefill branch, flash_attn_varlen_func

@@ -6,9 +6,12 @@ include/paged_kv.h). This package is the thin Python binding over it.
 from ._binding import (  # noqa: F401
     PKV_BF16,
     PKV_F32,
+    DecodeGraphs,
     PagedKVError,
+    attn_prefill_varlen,
     load_library,
     paged_attn_decode,
+    paged_attn_decode_store,
     paged_attn_decode_workspace_bytes,
     paged_attn_prefill_varlen,
     pkv_decode_metadata,
@@ -18,7 +21,8 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "PKV_BF16", "PKV_F32", "PagedKVError", "load_library", "paged_attn_decode",
+    "PKV_BF16", "PKV_F32", "DecodeGraphs", "PagedKVError", "attn_prefill_varlen",
+    "load_library", "paged_attn_decode", "paged_attn_decode_store",
     "paged_attn_decode_workspace_bytes", "paged_attn_prefill_varlen", "pkv_decode_metadata",
     "pkv_prefill_metadata", "pkv_status_string", "store_kvcache",
 ]

@@ -38,6 +38,14 @@ SIGNATURES = {
     "paged_attn_decode_store": (_c_int, [_p, _p, _p, _i64, _p, _i64, _p, _p, _p, _i32, _p, _i32,
                                          _p, _i32, _i32, _i32, _i32, _i32, _f, _c_int, _i32, _p,
                                          _size, _p]),
+    "pkv_decode_graphs_create": (_c_int, [ctypes.POINTER(_p), _i32, _p, _p, _p, _i64, _p, _i64,
+                                          _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32,
+                                          _i32, _f, _c_int, _i32, _p, _size]),
+    "pkv_decode_graphs_count": (_c_int, [_p]),
+    "pkv_decode_graphs_buckets": (_c_int, [_p, _p, _i32]),
+    "pkv_decode_graphs_bucket": (_c_int, [_p, _i32]),
+    "pkv_decode_graphs_launch": (_c_int, [_p, _i32, _p]),
+    "pkv_decode_graphs_destroy": (_c_int, [_p]),
     "attn_prefill_varlen": (_c_int, [_p, _p, _p, _i64, _p, _i64, _p, _p, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _i32, _f, _i32, _c_int, _p]),
     "paged_attn_prefill_varlen": (_c_int, [_p, _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32,
@@ -248,3 +256,68 @@ def attn_prefill_varlen(out, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, 
         _t_ptr(cu_seqlens_q), _t_ptr(cu_seqlens_k), B, T, int(max_seqlen_q), int(max_seqlen_k),
         Hq, Hkv, D, float(scale), 1 if causal else 0, _dtype_code(q), _stream(stream))
     _check("attn_prefill_varlen", rc)
+
+
+class DecodeGraphs:
+    """pkv_decode_graphs_*: one recorded paged_attn_decode_store call per batch bucket over
+    static device buffers sized for max_batch rows (the tensors are kept alive here, since
+    the graphs hold their addresses). ``launch(B)`` replays the smallest bucket >= B on the
+    stream; the caller has written rows 0 .. B-1 and padded rows B .. bucket-1 with
+    context_lens 0 and slot_mapping -1 (``pad`` does that)."""
+
+    def __init__(self, out, q, key, value, slot_mapping, k_cache, v_cache, block_tables,
+                 context_lens, scale, workspace, partition_size=0):
+        max_batch, Hq, D = q.shape
+        num_blocks, bs, Hkv, _ = k_cache.shape
+        if key.stride(2) != 1 or key.stride(1) != D or value.stride(2) != 1 or value.stride(1) != D:
+            raise ValueError("key/value need head stride head_dim and unit element stride")
+        self._keep = (out, q, key, value, slot_mapping, k_cache, v_cache, block_tables,
+                      context_lens, workspace)
+        self.slot_mapping, self.context_lens = slot_mapping, context_lens
+        ws_bytes = workspace.numel() * workspace.element_size()
+        h = _p()
+        rc = load_library().pkv_decode_graphs_create(
+            ctypes.byref(h), max_batch, _t_ptr(out), _t_ptr(q), _t_ptr(key), key.stride(0),
+            _t_ptr(value), value.stride(0), _t_ptr(slot_mapping), _t_ptr(k_cache),
+            _t_ptr(v_cache), num_blocks, _t_ptr(block_tables), block_tables.shape[1],
+            _t_ptr(context_lens), Hq, Hkv, D, bs, float(scale), _dtype_code(q), partition_size,
+            _t_ptr(workspace), ws_bytes)
+        _check("pkv_decode_graphs_create", rc)
+        self._h = h
+        self.max_batch = max_batch
+
+    @property
+    def buckets(self):
+        lib = load_library()
+        n = lib.pkv_decode_graphs_count(self._h)
+        _check("pkv_decode_graphs_count", min(n, 0))
+        arr = np.zeros(n, dtype=np.int32)
+        _check("pkv_decode_graphs_buckets", min(lib.pkv_decode_graphs_buckets(self._h, _np_ptr(arr), n), 0))
+        return [int(x) for x in arr]
+
+    def bucket(self, batch):
+        rc = load_library().pkv_decode_graphs_bucket(self._h, int(batch))
+        _check("pkv_decode_graphs_bucket", min(rc, 0))
+        return rc
+
+    def pad(self, batch):
+        """Rows batch .. bucket-1: context length 0 and slot -1 (enqueued on the current stream)."""
+        n = self.bucket(batch)
+        if n > batch:
+            self.context_lens[batch:n].zero_()
+            self.slot_mapping[batch:n].fill_(-1)
+
+    def launch(self, batch, stream=None):
+        _check("pkv_decode_graphs_launch",
+               load_library().pkv_decode_graphs_launch(self._h, int(batch), _stream(stream)))
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _check("pkv_decode_graphs_destroy", load_library().pkv_decode_graphs_destroy(self._h))
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -22,15 +22,33 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // The attention kernels move rows in 16-byte vector accesses.
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
-int decode_parts(int32_t max_blocks_per_seq, int32_t block_size, int32_t partition,
-                 int32_t* part_out, int64_t* max_parts_out) {
-  const int32_t part = partition == 0 ? pkv::kDecodeDefaultPartition : partition;
-  if (part < 64 || part > pkv::kDecodeMaxPartition || part % 64) return PKV_ERR_INVALID;
+// The library's smallest share when the caller passes 0: finer when the call can hold little
+// work (num_seqs * cap keys at most), so that a small batch still spreads over many
+// workgroups - a share of 256 keys leaves a batch-1 step streaming through a few of them.
+constexpr int64_t kFineShareKeys = 65536;     // below: 64-key shares
+constexpr int64_t kMediumShareKeys = 131072;  // up to: 128-key shares; above: the default
+int32_t default_partition(int64_t num_seqs, int64_t cap) {
+  const int64_t upper = num_seqs * cap;
+  if (upper < kFineShareKeys) return 64;
+  if (upper <= kMediumShareKeys) return 128;
+  return pkv::kDecodeDefaultPartition;
+}
+
+int decode_parts(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
+                 int32_t partition, int32_t* part_out, int64_t* max_parts_out) {
   const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
   if (cap > INT32_MAX) return PKV_ERR_INVALID;
+  const int32_t part = partition == 0 ? default_partition(num_seqs, cap) : partition;
+  if (part < 64 || part > pkv::kDecodeMaxPartition || part % 64) return PKV_ERR_INVALID;
   *part_out = part;
   *max_parts_out = ceil_div(cap, part) + 1;  // pieces a segment can be cut into
   return PKV_OK;
+}
+
+// Bytes of the partial slots and split metadata of one call.
+size_t decode_ws_bytes(int64_t num_seqs, int64_t num_heads, int64_t head_dim, int64_t max_parts) {
+  return (size_t)num_seqs * num_heads * max_parts * (head_dim + 2) * sizeof(float) +
+         ((size_t)num_seqs + 2) * sizeof(int32_t);
 }
 
 }  // namespace
@@ -171,11 +189,22 @@ size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, in
     return 0;
   int32_t part;
   int64_t max_parts;
-  if (decode_parts(max_blocks_per_seq, block_size, partition_size, &part, &max_parts) != PKV_OK)
+  if (decode_parts(num_seqs, max_blocks_per_seq, block_size, partition_size, &part, &max_parts) != PKV_OK)
     return 0;
-  const size_t partials = (size_t)num_seqs * num_heads * max_parts * (head_dim + 2) * sizeof(float);
-  const size_t meta = ((size_t)num_seqs + 2) * sizeof(int32_t);
-  return partials + meta;
+  size_t bytes = decode_ws_bytes(num_seqs, num_heads, head_dim, max_parts);
+  if (partition_size == 0) {
+    // the default share shrinks for fewer sequences, so a smaller call can need more slots
+    // per row: report the largest need of any call with at most num_seqs sequences, so that
+    // one workspace serves them all (the decode graphs record every bucket over one)
+    const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+    for (int64_t m : {(kFineShareKeys - 1) / cap, kMediumShareKeys / cap}) {
+      if (m < 1 || m >= num_seqs) continue;
+      const int64_t mp = ceil_div(cap, default_partition(m, cap)) + 1;
+      const size_t b = decode_ws_bytes(m, num_heads, head_dim, mp);
+      if (b > bytes) bytes = b;
+    }
+  }
+  return bytes;
 }
 
 }  // extern "C"
@@ -203,7 +232,7 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
     return PKV_ERR_UNSUPPORTED;
   int32_t part;
   int64_t max_parts;
-  if (decode_parts(max_blocks_per_seq, block_size, partition_size, &part, &max_parts) != PKV_OK)
+  if (decode_parts(num_seqs, max_blocks_per_seq, block_size, partition_size, &part, &max_parts) != PKV_OK)
     return PKV_ERR_INVALID;
   const int elem = dtype == PKV_BF16 ? 2 : 4;
   const int64_t row = (int64_t)num_kv_heads * head_dim;

@@ -7,6 +7,9 @@ arbitrary bits), makes the resident tokens resident with the library's own metad
 ``store_kvcache`` of the new tokens followed by ``paged_attn_decode`` or
 ``paged_attn_prefill_varlen``; ``step_fused()`` runs a decode step as one
 ``paged_attn_decode_store`` call. Host metadata is built by the library's host calls.
+``GraphDecodeStep`` replays decode steps of any subset of a ``DeviceStep``'s sequences from
+the library's recorded graphs, the way the engine's run_model does (static buffers, padded
+rows, the smallest bucket that fits).
 """
 from __future__ import annotations
 
@@ -138,3 +141,60 @@ class DeviceStep:
     def out_f64(self) -> np.ndarray:
         o = self.out.float().cpu().numpy() if self.out.dtype == torch.bfloat16 else self.out.cpu().numpy()
         return o.astype(np.float64)
+
+
+class GraphDecodeStep:
+    """Static buffers of max_batch rows over a DeviceStep's pool, with the library's decode
+    graphs recorded over them (``pkv_decode_graphs_*``). ``load(seqs)`` copies those
+    sequences' step inputs into the first rows and pads the rest of the bucket;
+    ``launch(batch)`` replays the bucket's graph."""
+
+    def __init__(self, ds: DeviceStep, max_batch: int, width: int = None):
+        w = ds.w
+        assert w.kind == "decode"
+        self.ds = ds
+        width = ds.block_tables.shape[1] if width is None else width
+        assert width >= ds.block_tables.shape[1]
+        dev = ds.q.device
+        Hq, D = ds.q.shape[1:]
+        Hkv = ds.new_k.shape[1]
+        self.out = torch.zeros(max_batch, Hq, D, dtype=ds.q.dtype, device=dev)
+        self.q = torch.zeros_like(self.out)
+        self.key = torch.zeros(max_batch, Hkv, D, dtype=ds.q.dtype, device=dev)
+        self.value = torch.zeros_like(self.key)
+        self.slots = torch.full((max_batch,), -1, dtype=torch.int32, device=dev)
+        self.ctx = torch.zeros(max_batch, dtype=torch.int32, device=dev)
+        # rows of padded sequences are never read; an out-of-range id makes that visible
+        self.tables = torch.full((max_batch, width), 1 << 30, dtype=torch.int32, device=dev)
+        nbytes = B.paged_attn_decode_workspace_bytes(max_batch, w.num_heads, w.head_dim, width,
+                                                     w.block_size, ds.partition_size)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.graphs = B.DecodeGraphs(self.out, self.q, self.key, self.value, self.slots,
+                                     ds.k_cache, ds.v_cache, self.tables, self.ctx, w.scale,
+                                     self.workspace, ds.partition_size)
+
+    def load(self, seqs):
+        ds, n = self.ds, len(seqs)
+        idx = torch.as_tensor(np.asarray(seqs), dtype=torch.long, device=ds.q.device)
+        self.q[:n] = ds.q[idx]
+        self.key[:n] = ds.new_k[idx]
+        self.value[:n] = ds.new_v[idx]
+        self.slots[:n] = ds.slot_mapping[idx]
+        self.ctx[:n] = ds.context_lens[idx]
+        self.tables[:n, :ds.block_tables.shape[1]] = ds.block_tables[idx]
+        self.graphs.pad(n)
+
+    def launch(self, batch, stream=None):
+        self.graphs.launch(batch, stream)
+        return self.out[:batch]
+
+    def eager(self, batch, out=None, stream=None):
+        """The recorded call, made eagerly on the same padded buffers (bucket rows)."""
+        n = self.graphs.bucket(batch)
+        out = self.out if out is None else out
+        ds = self.ds
+        B.paged_attn_decode_store(out[:n], self.q[:n], self.key[:n], self.value[:n],
+                                  self.slots[:n], ds.k_cache, ds.v_cache, self.tables[:n],
+                                  self.ctx[:n], ds.w.scale, workspace=self.workspace,
+                                  partition_size=ds.partition_size, stream=stream)
+        return out[:batch]

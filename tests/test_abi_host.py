@@ -200,7 +200,10 @@ def test_workspace_query():
         return B * Hq * slots * (D + 2) * 4 + (B + 2) * 4
     assert B.paged_attn_decode_workspace_bytes(4, 16, 128, 1, 256, 256) == expect(4, 16, 128, 1, 256, 256)
     assert B.paged_attn_decode_workspace_bytes(4, 16, 128, 16, 256, 256) == expect(4, 16, 128, 16, 256, 256)
-    assert B.paged_attn_decode_workspace_bytes(4, 16, 128, 16, 256, 0) == expect(4, 16, 128, 16, 256, 256)
+    # the default share: 64 keys below 65536 possible keys per call, 128 up to 131072, else 256
+    assert B.paged_attn_decode_workspace_bytes(4, 16, 128, 16, 256, 0) == expect(4, 16, 128, 16, 256, 64)
+    assert B.paged_attn_decode_workspace_bytes(32, 16, 128, 16, 256, 0) == expect(32, 16, 128, 16, 256, 128)
+    assert B.paged_attn_decode_workspace_bytes(64, 16, 128, 16, 256, 0) == expect(64, 16, 128, 16, 256, 256)
     assert B.paged_attn_decode_workspace_bytes(4, 16, 128, 16, 256, 100) == 0     # invalid partition
 
 
@@ -223,3 +226,40 @@ def _packed_rc(**kw):
 ])
 def test_packed_prefill_argument_validation(kw, status):
     assert _packed_rc(**kw) == status
+
+
+def test_decode_graphs_argument_validation():
+    # checks that come before any HIP call (no GPU needed)
+    lib = B.load_library()
+    h = ctypes.c_void_p()
+    args = [FAKE, FAKE, FAKE, 1024, FAKE, 1024, FAKE, FAKE, FAKE, 16, FAKE, 16, FAKE,
+            16, 8, 128, 256, 0.1, B.PKV_BF16, 0]
+    assert lib.pkv_decode_graphs_create(None, 4, *args, FAKE, 1 << 30) == -1
+    assert lib.pkv_decode_graphs_create(ctypes.byref(h), 0, *args, FAKE, 1 << 30) == -1
+    assert lib.pkv_decode_graphs_create(ctypes.byref(h), 16384, *args, FAKE, 1 << 30) == -1
+    assert lib.pkv_decode_graphs_create(ctypes.byref(h), 4, *args, FAKE, 16) == -3
+    assert lib.pkv_decode_graphs_create(ctypes.byref(h), 4, *args, None, 1 << 30) == -3
+    assert h.value is None
+    assert lib.pkv_decode_graphs_bucket(None, 1) == -1
+    assert lib.pkv_decode_graphs_count(None) == -1
+    assert lib.pkv_decode_graphs_buckets(None, None, 0) == -1
+    assert lib.pkv_decode_graphs_launch(None, 1, None) == -1
+    assert lib.pkv_decode_graphs_destroy(None) == -1
+
+
+@pytest.mark.parametrize("W,bs", [(16, 256), (12, 256), (3, 256), (40, 16), (1, 64)])
+def test_default_workspace_covers_every_smaller_batch(W, bs):
+    # one workspace sized for n sequences must serve any call with fewer (the decode graphs
+    # record every bucket over one): the default query is non-decreasing in n and covers
+    # the need of the default share at every n
+    def need(n):
+        cap = W * bs
+        upper = n * cap
+        part = 64 if upper < 65536 else (128 if upper <= 131072 else 256)
+        return n * 8 * (-(-cap // part) + 1) * (128 + 2) * 4 + (n + 2) * 4
+    prev = 0
+    for n in range(1, 700):
+        got = B.paged_attn_decode_workspace_bytes(n, 8, 128, W, bs, 0)
+        assert got >= prev and got >= need(n), n
+        assert got == max(need(m) for m in range(1, n + 1)), n
+        prev = got

@@ -1,0 +1,120 @@
+"""GPU parity of decode steps replayed from captured HIP graphs (pkv_decode_graphs_*).
+
+One pool holds the resident tokens of a batch of sequences; the graphs are recorded once
+over static buffers of max_batch rows. Each step copies a seeded subset of the sequences
+into the first B rows, pads the rest of its bucket (context 0, slot -1), replays, and is
+checked against the fp64 oracle and, bit for bit, against an eager paged_attn_decode_store
+on the same padded buffers. Replays are repeated with eager work and synchronisations
+between them, and the pool must end bit-identical to the one the separate store produces.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_225_amd import _binding as B
+from paged_kv_cache_225_amd.harness import DeviceStep, GraphDecodeStep
+from tests.oracle_pipeline import run_workload
+from tests.parity import assert_attention_close
+from workloads import make_config, make_decode
+
+pytestmark = pytest.mark.gpu
+
+W = 16  # static table width: 4096 tokens / 256
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def _run_steps(w, max_batch, batches, seed):
+    ds = DeviceStep(w, table_width=W)
+    st = GraphDecodeStep(ds, max_batch)
+    ref, _, _, _ = run_workload(w)
+    atol = 1e-4 if w.dtype == "f32" else 2e-2
+    l2 = 1e-5 if w.dtype == "f32" else 1e-2
+    rng = np.random.Generator(np.random.PCG64(seed))
+    stream = torch.cuda.current_stream()
+    for b in batches:
+        seqs = rng.choice(w.num_seqs, size=b, replace=False)
+        st.load(seqs)
+        bucket = st.graphs.bucket(b)
+        assert bucket >= b and bucket in st.graphs.buckets
+        st.out.fill_(float("nan"))
+        st.graphs.launch(b, stream)
+        torch.cuda.synchronize()
+        got = st.out[:b].double().cpu().numpy()
+        print(f"graph step batch {b} -> bucket {bucket}", flush=True)
+        assert_attention_close(got, ref[seqs], atol=atol, rel_l2=l2, label=f"graph batch {b}")
+        pad = st.out[b:bucket]
+        assert torch.equal(pad, torch.zeros_like(pad)), "padded rows must be zero"
+        # the same call eagerly on the same padded buffers: bit for bit
+        first = st.out[:bucket].clone()
+        eager = torch.empty_like(st.out)
+        st.eager(b, out=eager, stream=stream)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(eager[:bucket]), _bits(first)), "graph != eager"
+        # replays with eager work and synchronisations in between
+        for r in range(3):
+            st.out.fill_(float("nan"))
+            junk = torch.randn(256, 256, device=ds.q.device)
+            junk = junk @ junk
+            torch.cuda.synchronize()
+            st.graphs.launch(b, stream)
+            torch.cuda.synchronize()
+            assert torch.equal(_bits(st.out[:bucket]), _bits(first)), f"replay {r} differs"
+    return ds, st
+
+
+def test_graph_buckets_follow_the_engine_list():
+    w = make_decode(7, [5, 9], Hq=4, Hkv=2, D=64, dtype="f32")
+    ds = DeviceStep(w, table_width=W)
+    for max_batch, want in [(1, [1]), (6, [1, 2, 4, 6]), (16, [1, 2, 4, 8, 16]),
+                            (50, [1, 2, 4, 8, 16, 32, 48, 50]),
+                            (512, [1, 2, 4, 8] + list(range(16, 513, 16)))]:
+        st = GraphDecodeStep(ds, max_batch)
+        assert st.graphs.buckets == want
+        assert st.graphs.bucket(1) == 1
+        assert st.graphs.bucket(max_batch) == max_batch
+        with pytest.raises(B.PagedKVError):
+            st.graphs.bucket(max_batch + 1)
+        with pytest.raises(B.PagedKVError):
+            st.graphs.launch(0)
+        st.graphs.close()
+
+
+def test_graph_decode_qwen3_shapes():
+    # 64 sequences, the bench workload's head shapes, lengths mixing edge cases and U[256, 4096]
+    rng = np.random.Generator(np.random.PCG64(2024))
+    ctx = np.concatenate([[1, 2, 255, 256, 257, 4096, 4095, 513],
+                          rng.integers(256, 4096, size=56, endpoint=True)])
+    w = make_decode(31, ctx, Hq=16, Hkv=8, D=128, dtype="bf16", name="graph64")
+    ds, st = _run_steps(w, 64, [1, 3, 13, 16, 48, 64], seed=5)
+    # every sequence's newest token went through the fused store at least once (batch 64):
+    # the pool matches the one store_kvcache of all the step's tokens produces
+    sep = DeviceStep(w, table_width=W)
+    sep.store()
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(ds.k_cache), _bits(sep.k_cache))
+    assert torch.equal(_bits(ds.v_cache), _bits(sep.v_cache))
+
+
+def test_graph_decode_tiny_fp32():
+    w = make_config(1)
+    _run_steps(w, 2, [1, 2, 1], seed=9)
+
+
+def test_graph_decode_lengths_change_between_replays():
+    # the same recorded graph serves different context lengths: everything that depends on
+    # the data is computed on the device at replay time
+    w = make_decode(41, [4096, 300, 17, 2000, 1, 777, 3000, 64], Hq=16, Hkv=8, D=128,
+                    dtype="bf16", name="graph8")
+    ds = DeviceStep(w, table_width=W)
+    st = GraphDecodeStep(ds, 8)
+    ref, _, _, _ = run_workload(w)
+    for seqs in ([0, 1, 2, 3, 4, 5, 6, 7], [7, 6, 5, 4, 3, 2, 1, 0], [3, 1, 4, 0, 5, 7, 2, 6]):
+        st.load(seqs)
+        st.launch(8)
+        torch.cuda.synchronize()
+        assert_attention_close(st.out.double().cpu().numpy(), ref[seqs], label=f"rows {seqs}")

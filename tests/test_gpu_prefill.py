@@ -151,3 +151,18 @@ def test_prefill_loose_max_seqlen_k_is_bitwise_identical():
     assert torch.equal(a.view(torch.int16), ds.out.view(torch.int16))
     ref, _, _, _ = run_workload(w)
     assert_attention_close(ds.out_f64(), ref, rel_l2=1e-2, label="loose bound")
+
+
+def test_chunked_prefill_workload_full():
+    # the benchmarked chunked-prefill workload at full size: resident prefixes cut anywhere,
+    # so each chunk's store starts inside a block and every query row sits at Lk - Lq + i
+    from workloads import make_chunked_prefill
+    w = make_chunked_prefill()
+    assert (w.num_cached % w.block_size != 0).all()
+    ds = gpu_run(w)
+    ref, _, kc, vc = run_workload(w)
+    assert_attention_close(ds.out_f64(), ref, rel_l2=1e-2, label=w.name)
+    # the mid-block store leaves both pools bit-identical to the oracle's scatter
+    from tests.parity import oracle_bits, pool_bits
+    assert np.array_equal(pool_bits(ds.k_cache), oracle_bits(kc))
+    assert np.array_equal(pool_bits(ds.v_cache), oracle_bits(vc))

@@ -10,6 +10,8 @@ from .synth import (  # noqa: F401
     make_config,
     make_decode,
     make_prefill,
+    make_chunked_prefill,
+    CHUNKED_PREFILL_NAME,
     bf16_round_bits,
     BF16_POISON,
     F32_POISON,

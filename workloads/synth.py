@@ -264,3 +264,19 @@ def make_config(i: int, q_mult: float = 1.0) -> Workload:
                       Hkv=8, D=128, bs=bs, num_blocks=8192, scale=1.0 / np.sqrt(128.0),
                       shared_blocks=shared, n_prefix_blocks=8, q_mult=q_mult, meta=meta)
     raise ValueError(f"no config {i}")
+
+
+CHUNKED_PREFILL_NAME = "chunked_prefill_16seq_cached1_2048_chunk128_1024_bf16"
+
+
+def make_chunked_prefill(q_mult: float = 1.0) -> Workload:
+    """Chunked prefill (the engine's prefill of a long prompt in pieces): 16 sequences whose
+    first U{1..2048} tokens are already resident - cut anywhere, so the chunk's first token
+    usually falls inside a block - each computing a chunk of U{128..1024} more tokens; bf16,
+    16 q / 8 kv heads, head_dim 128, block 256. Structure and values from PCG64(1006)."""
+    rng = np.random.Generator(np.random.PCG64(1006))
+    cached = rng.integers(1, 2048, size=16, endpoint=True)
+    chunk = rng.integers(128, 1024, size=16, endpoint=True)
+    return _build(CHUNKED_PREFILL_NAME, "prefill", "bf16", rng, seq_lens=cached + chunk,
+                  num_cached=cached, Hq=16, Hkv=8, D=128, bs=256, num_blocks=1024,
+                  scale=1.0 / np.sqrt(128.0), q_mult=q_mult)
