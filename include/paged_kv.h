@@ -315,6 +315,70 @@ int attn_prefill_varlen(void* out, const void* q,
                         float scale, int32_t causal, pkv_dtype_t dtype,
                         hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------
+ * Host block manager with prefix caching - [P1] Block, BlockManager and Sequence listings
+ * and the Scheduler that calls them (schedule, preempt, postprocess); [P2] 请求执行 –
+ * 输入序列预处理与context构建 for what the tables and cached counts feed. Host memory only;
+ * nothing here touches the GPU. The manager owns its sequences (token ids, block table,
+ * cached and scheduled token counts), addressed by the id pkv_bm_add_sequence returns.
+ *
+ * Hash of a block: XXH64 (seed 0, the published xxHash algorithm) over the previous block's
+ * hash as 8 little-endian bytes (omitted for the first block, or when the previous block
+ * carries no hash) followed by the block's token ids as 64-bit little-endian integers.
+ * pkv_xxh64 and pkv_block_hash expose the two.
+ *
+ * Policy ([P1] BlockManager): free blocks sit on a FIFO; a used block's reference count is
+ * the number of tables holding it. pkv_bm_can_allocate(seq) walks the sequence's full
+ * blocks except its last, chaining the hash, while the index maps the hash to a block whose
+ * token ids are equal: it returns the number of such cache hits, or -1 when the FIFO holds
+ * fewer blocks than the table needs beyond its hits on used blocks. pkv_bm_allocate(seq, n)
+ * fills an empty table: the first n hits reuse their blocks (a used block gains a
+ * reference, a free one leaves the FIFO), the rest come off the FIFO's front (a block
+ * handed out drops its hash from the index and forgets its contents); the cached token
+ * count becomes n * block_size. pkv_bm_deallocate drops one reference per entry, last
+ * entry first; blocks reaching zero join the FIFO's back and keep their hash until handed
+ * out again. pkv_bm_can_append / pkv_bm_may_append: when the sequence's length is 1 modulo
+ * block_size (its newest token opens a block), one more free block is needed / appended.
+ * pkv_bm_set_scheduled records the step's token count (cached + scheduled <= length);
+ * pkv_bm_hash_blocks seals the blocks that cached + scheduled tokens complete, chaining from
+ * the previous block's hash, and indexes them; pkv_bm_commit_scheduled then adds the
+ * scheduled count to the cached count (the engine's postprocess order).
+ *
+ * Returns: counts or ids >= 0 where stated, else PKV_OK; PKV_ERR_INVALID for a null
+ * handle, an unknown or removed sequence id, a non-empty table for can_allocate / allocate,
+ * hits that are no longer hits or a FIFO too short for allocate, an empty FIFO for
+ * may_append, counts out of range, block_size < 2 or num_blocks < 1 for create.
+ * pkv_bm_block_table / pkv_bm_free_block_ids copy up to `capacity` ids and return the full
+ * count. pkv_bm_remove_sequence forgets a sequence whose table is empty.
+ * -------------------------------------------------------------------------------------*/
+typedef struct pkv_block_manager pkv_block_manager;
+
+uint64_t pkv_xxh64(const void* data, size_t len, uint64_t seed);
+int pkv_block_hash(const int64_t* token_ids, int32_t num_tokens, int32_t has_prefix,
+                   uint64_t prefix, uint64_t* hash_out);
+int pkv_bm_create(pkv_block_manager** handle, int32_t num_blocks, int32_t block_size);
+int pkv_bm_destroy(pkv_block_manager* handle);
+int pkv_bm_add_sequence(pkv_block_manager* handle, const int64_t* token_ids, int32_t num_tokens);
+int pkv_bm_append_token(pkv_block_manager* handle, int32_t seq, int64_t token_id);
+int pkv_bm_can_allocate(const pkv_block_manager* handle, int32_t seq);
+int pkv_bm_allocate(pkv_block_manager* handle, int32_t seq, int32_t num_cached_blocks);
+int pkv_bm_deallocate(pkv_block_manager* handle, int32_t seq);
+int pkv_bm_can_append(const pkv_block_manager* handle, int32_t seq);
+int pkv_bm_may_append(pkv_block_manager* handle, int32_t seq);
+int pkv_bm_set_scheduled(pkv_block_manager* handle, int32_t seq, int32_t num_scheduled_tokens);
+int pkv_bm_hash_blocks(pkv_block_manager* handle, int32_t seq);
+int pkv_bm_commit_scheduled(pkv_block_manager* handle, int32_t seq);
+int pkv_bm_sequence_info(const pkv_block_manager* handle, int32_t seq, int64_t* num_tokens,
+                         int64_t* num_cached_tokens, int64_t* num_scheduled_tokens,
+                         int32_t* table_len);
+int pkv_bm_block_table(const pkv_block_manager* handle, int32_t seq, int32_t* out,
+                       int32_t capacity);
+int pkv_bm_num_free_blocks(const pkv_block_manager* handle);
+int pkv_bm_free_block_ids(const pkv_block_manager* handle, int32_t* out, int32_t capacity);
+int pkv_bm_block_info(const pkv_block_manager* handle, int32_t block_id, int32_t* ref_count,
+                      int32_t* sealed, uint64_t* hash);
+int pkv_bm_remove_sequence(pkv_block_manager* handle, int32_t seq);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,6 +6,7 @@ include/paged_kv.h). This package is the thin Python binding over it.
 from ._binding import (  # noqa: F401
     PKV_BF16,
     PKV_F32,
+    BlockManager,
     DecodeGraphs,
     PagedKVError,
     attn_prefill_varlen,
@@ -14,15 +15,17 @@ from ._binding import (  # noqa: F401
     paged_attn_decode_store,
     paged_attn_decode_workspace_bytes,
     paged_attn_prefill_varlen,
+    pkv_block_hash,
     pkv_decode_metadata,
     pkv_prefill_metadata,
     pkv_status_string,
+    pkv_xxh64,
     store_kvcache,
 )
 
 __all__ = [
-    "PKV_BF16", "PKV_F32", "DecodeGraphs", "PagedKVError", "attn_prefill_varlen",
+    "PKV_BF16", "PKV_F32", "BlockManager", "DecodeGraphs", "PagedKVError", "attn_prefill_varlen",
     "load_library", "paged_attn_decode", "paged_attn_decode_store",
     "paged_attn_decode_workspace_bytes", "paged_attn_prefill_varlen", "pkv_decode_metadata",
-    "pkv_prefill_metadata", "pkv_status_string", "store_kvcache",
+    "pkv_block_hash", "pkv_prefill_metadata", "pkv_status_string", "pkv_xxh64", "store_kvcache",
 ]

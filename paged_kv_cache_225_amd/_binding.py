@@ -46,6 +46,26 @@ SIGNATURES = {
     "pkv_decode_graphs_bucket": (_c_int, [_p, _i32]),
     "pkv_decode_graphs_launch": (_c_int, [_p, _i32, _p]),
     "pkv_decode_graphs_destroy": (_c_int, [_p]),
+    "pkv_xxh64": (ctypes.c_uint64, [_p, _size, ctypes.c_uint64]),
+    "pkv_block_hash": (_c_int, [_p, _i32, _i32, ctypes.c_uint64, _p]),
+    "pkv_bm_create": (_c_int, [ctypes.POINTER(_p), _i32, _i32]),
+    "pkv_bm_destroy": (_c_int, [_p]),
+    "pkv_bm_add_sequence": (_c_int, [_p, _p, _i32]),
+    "pkv_bm_append_token": (_c_int, [_p, _i32, _i64]),
+    "pkv_bm_can_allocate": (_c_int, [_p, _i32]),
+    "pkv_bm_allocate": (_c_int, [_p, _i32, _i32]),
+    "pkv_bm_deallocate": (_c_int, [_p, _i32]),
+    "pkv_bm_can_append": (_c_int, [_p, _i32]),
+    "pkv_bm_may_append": (_c_int, [_p, _i32]),
+    "pkv_bm_set_scheduled": (_c_int, [_p, _i32, _i32]),
+    "pkv_bm_hash_blocks": (_c_int, [_p, _i32]),
+    "pkv_bm_commit_scheduled": (_c_int, [_p, _i32]),
+    "pkv_bm_sequence_info": (_c_int, [_p, _i32, _p, _p, _p, _p]),
+    "pkv_bm_block_table": (_c_int, [_p, _i32, _p, _i32]),
+    "pkv_bm_num_free_blocks": (_c_int, [_p]),
+    "pkv_bm_free_block_ids": (_c_int, [_p, _p, _i32]),
+    "pkv_bm_block_info": (_c_int, [_p, _i32, _p, _p, _p]),
+    "pkv_bm_remove_sequence": (_c_int, [_p, _i32]),
     "attn_prefill_varlen": (_c_int, [_p, _p, _p, _i64, _p, _i64, _p, _p, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _i32, _f, _i32, _c_int, _p]),
     "paged_attn_prefill_varlen": (_c_int, [_p, _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32,
@@ -314,6 +334,114 @@ class DecodeGraphs:
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:
             _check("pkv_decode_graphs_destroy", load_library().pkv_decode_graphs_destroy(self._h))
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def pkv_xxh64(data: bytes, seed: int = 0) -> int:
+    buf = ctypes.create_string_buffer(bytes(data), len(data))
+    return int(load_library().pkv_xxh64(buf, len(data), seed))
+
+
+def pkv_block_hash(token_ids, prefix=None) -> int:
+    """The chained block hash; ``prefix`` None = first block (no prefix bytes)."""
+    t = np.ascontiguousarray(token_ids, dtype=np.int64)
+    out = ctypes.c_uint64()
+    _check("pkv_block_hash", load_library().pkv_block_hash(
+        _np_ptr(t), len(t), 0 if prefix is None else 1, 0 if prefix is None else int(prefix),
+        ctypes.byref(out)))
+    return int(out.value)
+
+
+class BlockManager:
+    """pkv_bm_*: the native host block manager. Sequences are ids into the manager."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._lib = load_library()
+        h = _p()
+        _check("pkv_bm_create", self._lib.pkv_bm_create(ctypes.byref(h), num_blocks, block_size))
+        self._h = h
+        self.block_size = block_size
+        self.num_blocks = num_blocks
+
+    def _rc(self, fn, *args, allow_nonneg=False):
+        rc = getattr(self._lib, fn)(self._h, *args)
+        if rc < 0 or (rc > 0 and not allow_nonneg):
+            raise PagedKVError(fn, rc)
+        return rc
+
+    def add_sequence(self, token_ids) -> int:
+        t = np.ascontiguousarray(token_ids, dtype=np.int64)
+        return self._rc("pkv_bm_add_sequence", _np_ptr(t), len(t), allow_nonneg=True)
+
+    def append_token(self, seq, token_id):
+        self._rc("pkv_bm_append_token", seq, int(token_id))
+
+    def can_allocate(self, seq) -> int:
+        rc = self._lib.pkv_bm_can_allocate(self._h, seq)
+        if rc < -1:
+            raise PagedKVError("pkv_bm_can_allocate", rc)
+        return rc
+
+    def allocate(self, seq, num_cached_blocks):
+        self._rc("pkv_bm_allocate", seq, num_cached_blocks)
+
+    def deallocate(self, seq):
+        self._rc("pkv_bm_deallocate", seq)
+
+    def can_append(self, seq) -> bool:
+        return bool(self._rc("pkv_bm_can_append", seq, allow_nonneg=True))
+
+    def may_append(self, seq):
+        self._rc("pkv_bm_may_append", seq)
+
+    def set_scheduled(self, seq, n):
+        self._rc("pkv_bm_set_scheduled", seq, int(n))
+
+    def hash_blocks(self, seq):
+        self._rc("pkv_bm_hash_blocks", seq)
+
+    def commit_scheduled(self, seq):
+        self._rc("pkv_bm_commit_scheduled", seq)
+
+    def sequence_info(self, seq) -> dict:
+        nt, nc, ns, tl = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+        self._rc("pkv_bm_sequence_info", seq, ctypes.byref(nt), ctypes.byref(nc), ctypes.byref(ns),
+                 ctypes.byref(tl))
+        return {"num_tokens": nt.value, "num_cached_tokens": nc.value,
+                "num_scheduled_tokens": ns.value, "table_len": tl.value}
+
+    def block_table(self, seq) -> list:
+        n = self._rc("pkv_bm_block_table", seq, None, 0, allow_nonneg=True)
+        out = np.zeros(n, dtype=np.int32)
+        self._rc("pkv_bm_block_table", seq, _np_ptr(out), n, allow_nonneg=True)
+        return [int(x) for x in out]
+
+    def num_free_blocks(self) -> int:
+        return self._rc("pkv_bm_num_free_blocks", allow_nonneg=True)
+
+    def free_block_ids(self) -> list:
+        n = self.num_free_blocks()
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        self._rc("pkv_bm_free_block_ids", _np_ptr(out), n, allow_nonneg=True)
+        return [int(x) for x in out[:n]]
+
+    def block_info(self, block_id) -> tuple:
+        rc, sealed, h = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_uint64()
+        self._rc("pkv_bm_block_info", block_id, ctypes.byref(rc), ctypes.byref(sealed), ctypes.byref(h))
+        return rc.value, bool(sealed.value), int(h.value) if sealed.value else None
+
+    def remove_sequence(self, seq):
+        self._rc("pkv_bm_remove_sequence", seq)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.pkv_bm_destroy(self._h)
         self._h = None
 
     def __del__(self):

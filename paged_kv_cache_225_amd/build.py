@@ -1,7 +1,7 @@
 """Build libpaged_kv.so for gfx950 with hipcc, in-tree next to this file.
 
-Every .hip file under csrc/ is compiled to an object in parallel, then linked into one
-shared library. Packed fp32 instructions are disabled for the device code.
+Every .hip file (and host-only .cpp file) under csrc/ is compiled to an object in
+parallel, then linked into one shared library. Packed fp32 instructions are disabled for the device code.
 Run as ``python -m paged_kv_cache_225_amd.build``.
 """
 from __future__ import annotations
@@ -47,7 +47,7 @@ def _compile(src: str, obj_dir: str) -> str:
 
 
 def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     obj_dir = os.path.join(ROOT, "_build")
     os.makedirs(obj_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
