@@ -253,6 +253,31 @@ def bench_graph_decode(torch, iters):
             "steps": rows}
 
 
+def bench_sampler(torch, iters):
+    """Temperature sampling of one decode step's next tokens: 64 rows of Qwen3-vocabulary
+    (151936) fp32 logits, the row's logits read once (HBM bytes = rows x vocab x 4)."""
+    from paged_kv_cache_225_amd import _binding as B
+    rows, vocab = 64, 151936
+    g = torch.Generator(device="cuda").manual_seed(5)
+    logits = torch.randn(rows, vocab, device="cuda", generator=g) * 3
+    temps = torch.full((rows,), 0.6, device="cuda")
+    tokens = torch.empty(rows, dtype=torch.int32, device="cuda")
+    ws = torch.empty(B.pkv_sample_workspace_bytes(rows, vocab), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    step = [0]
+
+    def call():
+        step[0] += 1
+        B.pkv_sample(tokens, logits, temps, 1234, step[0], workspace=ws, stream=stream)
+
+    med, p10, p90 = _median_event_ms(torch, call, iters, 5, stream)
+    nbytes = rows * vocab * 4
+    return {"workload": "sampler_64rows_vocab151936_f32", "us_median": med * 1e3,
+            "us_p10_p90": [p10 * 1e3, p90 * 1e3], "logit_bytes": nbytes,
+            "gbs": nbytes / (med * 1e-3) / 1e9, "frac_hbm": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "bound": "alu (a Philox4x64-10 block per 8 elements and two logs per element)"}
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b64_hbm_traffic.json")
 
 
@@ -334,7 +359,7 @@ def main():
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
                     help="copy: run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--only", choices=["prefill3", "prefill4", "prefill3packed", "chunked", "large",
-                                       "graph"], default=None,
+                                       "graph", "sampler"], default=None,
                     help="run one secondary workload alone (for profiler passes)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -359,6 +384,8 @@ def main():
             res = bench_prefill(torch, "chunked", args.iters, 5)
         elif args.only == "graph":
             res = bench_graph_decode(torch, 200)
+        elif args.only == "sampler":
+            res = bench_sampler(torch, args.iters)
         else:
             res = bench_prefill(torch, 3 if args.only == "prefill3" else 4, args.iters, 5)
         print(json.dumps({"only": args.only, **res}), flush=True)
@@ -401,6 +428,8 @@ def main():
         line["large_decode"] = bench_large_decode(torch, args.iters, 5)
         print("bench: graph-replayed small-batch decode", file=sys.stderr, flush=True)
         line["graph_decode"] = bench_graph_decode(torch, 200)
+        print("bench: sampler", file=sys.stderr, flush=True)
+        line["sampler"] = bench_sampler(torch, args.iters)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

@@ -316,6 +316,33 @@ int attn_prefill_varlen(void* out, const void* q,
                         hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * Temperature sampling - [P3] section 4.3 采样器 (Sampler.forward); [P1] SamplingParams
+ * (temperature > 1e-10) and ModelRunner.prepare_sample / run (one temperature per row).
+ * For each row r: tokens[r] = argmax_i softmax(logits[r] / T_r)_i / max(E_ri, 1e-10) with
+ * E_ri ~ Exp(1) independent, i.e. a draw from softmax(logits[r] / T_r). Computed as the
+ * first index of the largest s_i = logits[r, i] / T_r - log(max(E_ri, 1e-10)) (the softmax
+ * denominator does not change the winner).
+ * E_ri = -log(u), u = (b + 0.5) / 2^23, b = the top 23 bits of a 32-bit word of
+ * Philox4x64-10 (Salmon et al., SC 2011) with key (seed, 0) and counter (i / 8, r, offset,
+ * 0): word (i % 8) / 2 of the block, low half for even i, high half for odd i. The caller
+ * advances `offset` (e.g. once per step) for fresh draws with one seed.
+ *   tokens       device int32 [num_rows] (output)
+ *   logits       device [num_rows, row_stride] (first vocab_size columns used), fp32 or bf16;
+ *                rows starting on 16 bytes are read with vector loads, others element-wise
+ *   temperatures device fp32 [num_rows], each > 0
+ *   workspace    device, >= pkv_sample_workspace_bytes(num_rows, vocab_size), 16-byte aligned
+ * Scores are fp32 (the kernel's precision): among candidates whose scores differ by less
+ * than fp32 rounding, either may be returned. NaN logits never win; a row with no finite
+ * score returns 0. num_rows == 0 is a no-op.
+ * Errors: PKV_ERR_INVALID (null pointers, row_stride < vocab_size),
+ * PKV_ERR_UNSUPPORTED (dtype, num_rows > 65535), PKV_ERR_WORKSPACE, PKV_ERR_HIP.
+ * -------------------------------------------------------------------------------------*/
+size_t pkv_sample_workspace_bytes(int32_t num_rows, int32_t vocab_size);
+int pkv_sample(int32_t* tokens, const void* logits, int64_t row_stride, int32_t num_rows,
+               int32_t vocab_size, pkv_dtype_t dtype, const float* temperatures, uint64_t seed,
+               uint64_t offset, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * Host block manager with prefix caching - [P1] Block, BlockManager and Sequence listings
  * and the Scheduler that calls them (schedule, preempt, postprocess); [P2] 请求执行 –
  * 输入序列预处理与context构建 for what the tables and cached counts feed. Host memory only;

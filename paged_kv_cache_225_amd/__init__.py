@@ -18,6 +18,8 @@ from ._binding import (  # noqa: F401
     pkv_block_hash,
     pkv_decode_metadata,
     pkv_prefill_metadata,
+    pkv_sample,
+    pkv_sample_workspace_bytes,
     pkv_status_string,
     pkv_xxh64,
     store_kvcache,
@@ -27,5 +29,6 @@ __all__ = [
     "PKV_BF16", "PKV_F32", "BlockManager", "DecodeGraphs", "PagedKVError", "attn_prefill_varlen",
     "load_library", "paged_attn_decode", "paged_attn_decode_store",
     "paged_attn_decode_workspace_bytes", "paged_attn_prefill_varlen", "pkv_decode_metadata",
-    "pkv_block_hash", "pkv_prefill_metadata", "pkv_status_string", "pkv_xxh64", "store_kvcache",
+    "pkv_block_hash", "pkv_prefill_metadata", "pkv_sample", "pkv_sample_workspace_bytes",
+    "pkv_status_string", "pkv_xxh64", "store_kvcache",
 ]

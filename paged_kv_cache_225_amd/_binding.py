@@ -46,6 +46,9 @@ SIGNATURES = {
     "pkv_decode_graphs_bucket": (_c_int, [_p, _i32]),
     "pkv_decode_graphs_launch": (_c_int, [_p, _i32, _p]),
     "pkv_decode_graphs_destroy": (_c_int, [_p]),
+    "pkv_sample_workspace_bytes": (_size, [_i32, _i32]),
+    "pkv_sample": (_c_int, [_p, _p, _i64, _i32, _i32, _c_int, _p, ctypes.c_uint64, ctypes.c_uint64,
+                            _p, _size, _p]),
     "pkv_xxh64": (ctypes.c_uint64, [_p, _size, ctypes.c_uint64]),
     "pkv_block_hash": (_c_int, [_p, _i32, _i32, ctypes.c_uint64, _p]),
     "pkv_bm_create": (_c_int, [ctypes.POINTER(_p), _i32, _i32]),
@@ -449,3 +452,21 @@ class BlockManager:
             self.close()
         except Exception:
             pass
+
+
+def pkv_sample_workspace_bytes(num_rows, vocab_size) -> int:
+    return int(load_library().pkv_sample_workspace_bytes(num_rows, vocab_size))
+
+
+def pkv_sample(tokens, logits, temperatures, seed, offset=0, workspace=None, stream=None):
+    """tokens int32 [B] (out); logits [B, >= V] fp32/bf16 (V = logits.shape[1] unless a wider
+    row stride is viewed); temperatures fp32 [B]; workspace: >= the queried bytes."""
+    B, V = logits.shape
+    if logits.stride(1) != 1:
+        raise ValueError("logits need unit element stride")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().pkv_sample(_t_ptr(tokens), _t_ptr(logits), logits.stride(0), B, V,
+                                   _dtype_code(logits), _t_ptr(temperatures),
+                                   int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
+                                   _t_ptr(workspace), ws_bytes, _stream(stream))
+    _check("pkv_sample", rc)
