@@ -314,3 +314,111 @@ def test_native_argument_errors():
     m.remove_sequence(s2)
     with pytest.raises(B.PagedKVError):
         m.block_table(s2)
+
+
+# ------------------------------------------------------------------ planted mistakes
+def _pin_battery():
+    """Run the oracle pins above; return how many fail."""
+    fails = 0
+    for t in (test_oracle_prefix_hit_shares_and_revives_blocks,
+              test_oracle_last_block_is_never_a_hit_and_needs_free_blocks,
+              test_oracle_handing_out_a_freed_block_evicts_its_hash,
+              test_oracle_token_check_guards_the_hash_index,
+              test_oracle_growth_rule_at_block_boundaries,
+              test_oracle_seal_chains_from_the_previous_block_across_steps,
+              test_oracle_free_hits_need_free_blocks):
+        try:
+            t()
+        except (AssertionError, KeyError, IndexError, ValueError):
+            fails += 1
+    return fails
+
+
+def test_oracle_free_hits_need_free_blocks():
+    # a hit on a free block still takes that block off the free list, so it counts
+    # against the free blocks a sequence needs
+    m = BlockManagerOracle(4, 4)
+    a = SeqState(range(9))                      # blocks [0..3] [4..7] [8]
+    m.admit(a, m.probe(a))
+    _prefill_all(m, a)
+    m.retire(a)                                 # all free again, two of them sealed
+    x = SeqState(range(100, 105))               # takes 2 blocks off the front
+    m.admit(x, m.probe(x))
+    assert len(m.fifo) == 2
+    b = SeqState(list(range(8)) + [50, 51, 52, 53, 54])  # 2 free hits + 2 new = 4 > 2
+    assert m.probe(b) == -1
+
+
+def _mutant(kind):
+    class Mutant(BlockManagerOracle):
+        pass
+    if kind == "release_to_front":
+        def _push_free(self, bid):
+            self.in_use.discard(bid)
+            self.fifo.appendleft(bid)
+        Mutant._push_free = _push_free
+    elif kind == "unchained_hash":
+        import oracle.block_manager as OB
+        def seal(self, s):
+            first, last = s.num_cached // self.bs, (s.num_cached + s.num_scheduled) // self.bs
+            for i in range(first, last):
+                toks = s.block_tokens(i, self.bs)
+                h = OB.block_hash(toks)             # the chain dropped
+                self.seal_hash[s.table[i]] = h
+                self.seal_tokens[s.table[i]] = toks
+                self.index[h] = s.table[i]
+        Mutant.seal = seal
+    elif kind == "last_block_can_hit":
+        def _hits(self, s):
+            out, h = [], None
+            for i in range(s.nblocks(self.bs)):    # walks the last block too
+                toks = s.block_tokens(i, self.bs)
+                h = block_hash(toks, h)
+                bid = self.index.get(h)
+                if bid is None or self.seal_tokens[bid] != toks:
+                    break
+                out.append(bid)
+            return out
+        Mutant._hits = _hits
+    elif kind == "free_hits_cost_nothing":
+        def probe(self, s):
+            hits = self._hits(s)
+            need = s.nblocks(self.bs) - len(hits)
+            return -1 if len(self.fifo) < need else len(hits)
+        Mutant.probe = probe
+    elif kind == "grow_on_full_block":
+        def grow(self, s):
+            if len(s.tokens) % self.bs == 0:
+                s.table.append(self._pop_free())
+        def room_to_grow(self, s):
+            return len(self.fifo) >= (1 if len(s.tokens) % self.bs == 0 else 0)
+        Mutant.grow = grow
+        Mutant.room_to_grow = room_to_grow
+    elif kind == "reuse_keeps_hash":
+        def _pop_free(self):
+            bid = self.fifo.popleft()
+            self.refs[bid] = 1
+            self.in_use.add(bid)
+            return bid
+        Mutant._pop_free = _pop_free
+    elif kind == "no_token_check":
+        def _hits(self, s):
+            out, h = [], None
+            for i in range(s.nblocks(self.bs) - 1):
+                h = block_hash(s.block_tokens(i, self.bs), h)
+                bid = self.index.get(h)
+                if bid is None:
+                    break
+                out.append(bid)
+            return out
+        Mutant._hits = _hits
+    return Mutant
+
+
+@pytest.mark.parametrize("kind", ["release_to_front", "unchained_hash", "last_block_can_hit",
+                                  "free_hits_cost_nothing", "grow_on_full_block",
+                                  "reuse_keeps_hash", "no_token_check"])
+def test_planted_mistake_in_the_block_manager_oracle_is_caught(kind, monkeypatch):
+    assert _pin_battery() == 0
+    monkeypatch.setitem(globals(), "BlockManagerOracle", _mutant(kind))
+    assert _pin_battery() >= 1, kind

@@ -88,3 +88,42 @@ def test_sample_argument_validation():
     assert rc(stride=999) == -1                      # row shorter than the vocabulary
     assert rc(dt=7) == -2 and rc(rows=70000) == -2
     assert rc(ws_bytes=ws - 1) == -3 and rc(ws=None) == -3
+
+
+# ------------------------------------------------------------------ planted mistakes
+def _sampler_pins():
+    fails = 0
+    for t in (test_sampler_draws_follow_softmax_of_tempered_logits, test_tiny_temperature_is_argmax,
+              test_exponential_draws_are_exp1):
+        try:
+            t()
+        except AssertionError:
+            fails += 1
+    return fails
+
+
+@pytest.mark.parametrize("kind", ["temperature_multiplies", "multiplies_by_draw", "uniform_not_exp",
+                                  "no_softmax_temperature"])
+def test_planted_mistake_in_the_sampler_oracle_is_caught(kind, monkeypatch):
+    import oracle.sampler as OS
+    assert _sampler_pins() == 0
+    real_draws, real_sample = OS.exp_draws, OS.sample
+
+    def sample(logits, temperatures, seed, offset=0):
+        l = OS._to_f64(logits)
+        T = np.asarray(temperatures, dtype=np.float64)
+        z = l * T[:, None] if kind == "temperature_multiplies" else (
+            l if kind == "no_softmax_temperature" else l / T[:, None])
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        E = np.maximum(OS.exp_draws(l.shape[0], l.shape[1], seed, offset), 1e-10)
+        return np.argmax(p * E if kind == "multiplies_by_draw" else p / E, axis=1)
+
+    def exp_draws(num_rows, vocab, seed, offset):
+        E = real_draws(num_rows, vocab, seed, offset)
+        return np.exp(-E) if kind == "uniform_not_exp" else E   # u instead of -log(u)
+
+    monkeypatch.setattr(OS, "exp_draws", exp_draws)
+    monkeypatch.setitem(globals(), "exp_draws", exp_draws)
+    monkeypatch.setitem(globals(), "sample", sample)
+    assert _sampler_pins() >= 1, kind
