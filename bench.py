@@ -243,13 +243,17 @@ def bench_graph_decode(torch, iters):
             t0 = time.perf_counter()
             for _ in range(iters):
                 fn()
+            t_host = time.perf_counter() - t0
             torch.cuda.synchronize()
             res[name + "_us_per_step"] = (time.perf_counter() - t0) / iters * 1e6
+            # host time to enqueue a step (the loop's own cost, before waiting for the GPU)
+            res[name + "_host_us_per_step"] = t_host / iters * 1e6
         rows.append(res)
     return {"workload": "decode steps of 1/4/16/64 sequences from the batch-64 workload "
                         "(ctx U[256,4096], 16q/8kv heads, d128, bf16)",
             "note": "wall time per step over back-to-back steps, both legs on the same "
-                    "buffers; a small batch's K/V stays in the last-level cache across steps",
+                    "buffers; a small batch's K/V stays in the last-level cache across steps; "
+                    "host_us: the enqueue loop's time per step before the final wait",
             "steps": rows}
 
 
