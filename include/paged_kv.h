@@ -41,7 +41,7 @@ typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype_t;
 enum {
   PKV_OK = 0,
   PKV_ERR_INVALID = -1,     /* null pointer, negative size, inconsistent arguments */
-  PKV_ERR_UNSUPPORTED = -2, /* a valid shape or dtype this build does not implement */
+  PKV_ERR_UNSUPPORTED = -2, /* a valid shape or dtype the library does not implement */
   PKV_ERR_WORKSPACE = -3,   /* decode workspace smaller than the query function asks */
   PKV_ERR_HIP = -4          /* a HIP launch error */
 };

@@ -15,7 +15,7 @@ i, high half for odd i); its top 23 bits b give u = (b + 0.5) / 2^23 and E = -lo
 
 ``sample`` follows the pages literally in fp64 (softmax, then the quotient); ``scores``
 gives the fp64 log of the quotient up to a per-row constant, l / T - log(max(E, 1e-10)),
-which the tests use to judge near-ties.
+which the tests use to decide near-ties.
 
 Pins (tests/test_sampler.py): ``philox4x64_10`` equals numpy's Philox bit generator; the
 empirical frequencies of many draws match softmax(l / T); a tiny temperature returns the

@@ -221,7 +221,7 @@ def make_prefill(seed, q_lens, cached=None, *, Hq, Hkv, D, dtype="bf16", bs=256,
 
 
 def make_config(i: int, q_mult: float = 1.0) -> Workload:
-    """The five workloads the path is measured on (sizes from the benchmark's configs).
+    """The five workloads the path is measured on (their stated sizes and distributions).
 
     Structure and values come from PCG64(1000 + i).
     """
