@@ -11,6 +11,7 @@ import json
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -263,3 +264,10 @@ def test_default_workspace_covers_every_smaller_batch(W, bs):
         assert got >= prev and got >= need(n), n
         assert got == max(need(m) for m in range(1, n + 1)), n
         prev = got
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the library has one-GPU kernels only; bench.py says so and exits before touching a GPU
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
