@@ -347,36 +347,51 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
             m_run[nt] = m_new;
           }
         }
-  #pragma unroll
-        for (int nt = 0; nt < GH; ++nt) {
-          const float mc = (m_run[nt] == -INFINITY ? 0.f : m_run[nt]) * scale_log2e;
-          float pv[4][4];
-  #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-  #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              pv[mt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][nt][r], scale_log2e, -mc));
-  #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            u32x4_t w;
-            w.x = pack_bf16x2(pv[2 * ks][0], pv[2 * ks][1]);
-            w.y = pack_bf16x2(pv[2 * ks][2], pv[2 * ks][3]);
-            w.z = pack_bf16x2(pv[2 * ks + 1][0], pv[2 * ks + 1][1]);
-            w.w = pack_bf16x2(pv[2 * ks + 1][2], pv[2 * ks + 1][3]);
-            pb[ks][nt] = __builtin_bit_cast(bf16x8_t, w);
-          }
-        }
       };
       if (kt * kBK + kBK - 1 > wave_min_pos)
         softmax(std::true_type{});
       else
         softmax(std::false_type{});
 
+      // Probabilities 2^(s scale log2e - m) of the lane's keys, rounded to bf16 in the PV
+      // operand layout. Those of the second 32 keys (ks = 1) are computed in pieces between
+      // the MFMAs of the first 32 keys' PV product, which do not depend on them, so the
+      // wavefront's own matrix and vector work overlap.
+      float mcs[GH];
+      float pv[GH][4][4];
+  #pragma unroll
+      for (int nt = 0; nt < GH; ++nt)
+        mcs[nt] = (m_run[nt] == -INFINITY ? 0.f : m_run[nt]) * scale_log2e;
+      auto prob = [&](int nt, int mt, int r) {
+        pv[nt][mt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][nt][r], scale_log2e, -mcs[nt]));
+      };
+      auto pack = [&](int ks) {
+  #pragma unroll
+        for (int nt = 0; nt < GH; ++nt) {
+          u32x4_t w;
+          w.x = pack_bf16x2(pv[nt][2 * ks][0], pv[nt][2 * ks][1]);
+          w.y = pack_bf16x2(pv[nt][2 * ks][2], pv[nt][2 * ks][3]);
+          w.z = pack_bf16x2(pv[nt][2 * ks + 1][0], pv[nt][2 * ks + 1][1]);
+          w.w = pack_bf16x2(pv[nt][2 * ks + 1][2], pv[nt][2 * ks + 1][3]);
+          pb[ks][nt] = __builtin_bit_cast(bf16x8_t, w);
+        }
+      };
+  #pragma unroll
+      for (int nt = 0; nt < GH; ++nt)
+  #pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) prob(nt, mt, r);
+      pack(0);
+      constexpr int kLate = GH * 2 * 4;             // probabilities of the second 32 keys
+      constexpr int kPerStep = (kLate + DT - 1) / DT;  // computed after each of the DT steps
+
       // O^T += V^T P^T ; lane (row d = 16 i + col, group quad) reads keys 32 ks + 4 quad + 0..3
       // and 32 ks + 16 + 4 quad + 0..3 with two transposing reads. Source lane L of a group
       // points at key k0 + L / 4, dims 16 i + 4 (L % 4) .. + 3.
   #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < 2; ++ks) {
+        if (ks == 1) pack(1);
   #pragma unroll
         for (int i = 0; i < DT; ++i) {
           s16x4_t part[2];
@@ -395,7 +410,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
           const bf16x8_t av = __builtin_bit_cast(bf16x8_t, w);
   #pragma unroll
           for (int nt = 0; nt < GH; ++nt) oacc[i][nt] = mfma16(av, pb[ks][nt], oacc[i][nt]);
+          if (ks == 0) {
+  #pragma unroll
+            for (int e = i * kPerStep; e < (i + 1) * kPerStep && e < kLate; ++e)
+              prob(e / 8, 2 + (e / 4) % 2, e % 4);
+          }
         }
+      }
       const bf16x8_t ones = __builtin_bit_cast(
           bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   #pragma unroll
