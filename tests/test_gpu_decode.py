@@ -79,6 +79,32 @@ def test_decode_partition_sizes(part):
     assert torch.equal(first.view(torch.int16), ds.out.view(torch.int16)), "not deterministic"
 
 
+# One segment cut into ~141 pieces (64-key shares over a 9000-key sequence): the combine
+# merges its slots 64 at a time, so the rounds past the first 64 slots run.
+LONG = [
+    # (dtype, D, Hq, Hkv, fused): Hkv 8 gives workgroup-owned shares of whole token rows,
+    # Hkv 2 wavefront-owned shares over (sequence, kv head) segments
+    ("bf16", 128, 16, 8, False),
+    ("bf16", 128, 16, 8, True),
+    ("f32", 64, 4, 2, False),
+    ("f32", 64, 4, 2, True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(LONG)))
+def test_decode_segment_of_more_than_64_pieces(case):
+    dtype, D, Hq, Hkv, fused = LONG[case]
+    w = make_decode(210 + case, [9000, 5, 300, 4160], Hq=Hq, Hkv=Hkv, D=D, dtype=dtype,
+                    bs=256, name=f"long{case}")
+    print(f"case {case}: {dtype} D {D} Hq {Hq} Hkv {Hkv} fused {fused}", flush=True)
+    ds = DeviceStep(w, partition_size=64)
+    (ds.step_fused if fused else ds.step)()
+    torch.cuda.synchronize()
+    ref, _, _, _ = run_workload(w)
+    atol, l2 = (1e-4, 1e-5) if dtype == "f32" else (2e-2, 1e-2)
+    assert_attention_close(ds.out_f64(), ref, atol=atol, rel_l2=l2, label=w.name)
+
+
 def test_decode_peaked_logits():
     w = make_config(2, q_mult=4.0)
     check(w)

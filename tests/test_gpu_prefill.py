@@ -54,6 +54,26 @@ def test_prefill_configs_full(cfg):
     print(f"config {cfg}: {st}", flush=True)
 
 
+# Long prefixes: a few hundred key tiles per unit (hundreds of grid planes), tables of
+# hundreds of blocks (block 16), a one-query row over 16000 cached keys, and a sequence with
+# no prefix beside them.
+LONG = [
+    # (D, Hq, Hkv, bs, q_lens, cached)
+    (128, 16, 8, 256, [300, 1, 64], [12000, 16000, 0]),
+    (128, 16, 8, 16, [130, 2], [7000, 8191]),
+    (64, 16, 2, 64, [200, 65], [9999, 4096]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(LONG)))
+def test_prefill_long_prefixes(case):
+    D, Hq, Hkv, bs, ql, cached = LONG[case]
+    print(f"case {case}: D {D} Hq {Hq} Hkv {Hkv} bs {bs} q {ql} cached {cached}", flush=True)
+    w = make_prefill(320 + case, ql, cached=cached, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16", bs=bs,
+                     name=f"long{case}")
+    check(w)
+
+
 def test_prefill_peaked_logits():
     check(make_config(3, q_mult=4.0))
 
