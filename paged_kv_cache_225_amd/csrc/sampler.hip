@@ -37,14 +37,28 @@ struct U64x4 {
   uint64_t x[4];
 };
 
+// The 128-bit product m * x as (hi, lo), from four 32 x 32 -> 64-bit multiply-adds that
+// the high and low halves share (every partial sum below fits in 64 bits). 32-bit integer
+// products run at a quarter of the vector rate, so they set the kernel's time.
+__device__ __forceinline__ void mulhilo64(uint64_t m, uint64_t x, uint64_t& hi, uint64_t& lo) {
+  const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
+  const uint32_t xl = (uint32_t)x, xh = (uint32_t)(x >> 32);
+  const uint64_t p00 = (uint64_t)ml * xl;
+  const uint64_t t = (uint64_t)ml * xh + (p00 >> 32);
+  const uint64_t u = (uint64_t)mh * xl + (uint32_t)t;
+  hi = (uint64_t)mh * xh + (t >> 32) + (u >> 32);
+  lo = (u << 32) | (uint32_t)p00;
+}
+
 __device__ __forceinline__ U64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2,
                                               uint64_t c3, uint64_t k0, uint64_t k1) {
   constexpr uint64_t kM0 = 0xD2E7470EE14C6C93ULL, kM1 = 0xCA5A826395121157ULL;
   constexpr uint64_t kW0 = 0x9E3779B97F4A7C15ULL, kW1 = 0xBB67AE8584CAA73BULL;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint64_t hi0 = __umul64hi(kM0, c0), lo0 = kM0 * c0;
-    const uint64_t hi1 = __umul64hi(kM1, c2), lo1 = kM1 * c2;
+    uint64_t hi0, lo0, hi1, lo1;
+    mulhilo64(kM0, c0, hi0, lo0);
+    mulhilo64(kM1, c2, hi1, lo1);
     const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0;
     c1 = lo1;
@@ -61,13 +75,26 @@ __device__ __forceinline__ bool better(float s, int i, float bs, int bi) {
   return s > bs || (s == bs && i < bi);
 }
 
-// u = (top 23 bits + 0.5) / 2^23 is exact in fp32 and lies in [2^-24, 1 - 2^-24]; the
-// accurate logf keeps E = -log(u) to ~1 ulp also near u = 1, where E is small and the
-// element most likely to win (a fast log would lose E's relative accuracy there).
+// Natural log of a positive, normal, finite float: the hardware base-2 log times ln 2, with
+// ln 2 split in two floats and the product's rounding error kept by an fma, so the result
+// stays within about an ulp also where it is small (x near 1). Denormal, zero and infinite
+// inputs are not handled: the callers' arguments are never such.
+__device__ __forceinline__ float log_normal(float x) {
+  constexpr float kLn2Hi = 0x1.62e43p-1f;     // ln 2 rounded to float
+  constexpr float kLn2Lo = -0x1.05c61p-29f;   // ln 2 - kLn2Hi, rounded to float
+  const float r = __builtin_amdgcn_logf(x);   // log2(x)
+  const float hi = r * kLn2Hi;
+  return hi + fmaf(r, kLn2Lo, fmaf(r, kLn2Hi, -hi));
+}
+
+// u = (top 23 bits + 0.5) / 2^23 is exact in fp32 and lies in [2^-24, 1 - 2^-24], so
+// E = -log(u) lies in [6e-8, 16.7]: both logs take normal arguments. E keeps ~1 ulp also
+// near u = 1, where it is small and the element most likely to win (a log accurate only in
+// absolute terms would lose E's relative accuracy there).
 __device__ __forceinline__ float score_of(float logit, float inv_t, uint32_t bits) {
   const float u = ((float)(bits >> 9) + 0.5f) * (1.0f / 8388608.0f);
-  const float e = fmaxf(-logf(u), 1e-10f);
-  return logit * inv_t - logf(e);
+  const float e = fmaxf(-log_normal(u), 1e-10f);
+  return logit * inv_t - log_normal(e);
 }
 
 template <typename T>
