@@ -271,3 +271,29 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_decode_traffic_record_is_consistent(monkeypatch):
+    # The bench's roofline `traffic` comes from the committed rocprofv3 counter record: it
+    # must equal the record's own FETCH/WRITE KiB scaled by its copy calibration, sit a few
+    # percent above the algorithmic bytes (the split-K partials; no K/V byte read twice),
+    # and be reported only while the decode sources are the ones the counters were taken on.
+    sys.path.insert(0, ROOT)
+    import bench
+    with open(bench.TRAFFIC_FILE) as fh:
+        rec = json.load(fh)
+    cal = rec["calibration"]
+    assert cal["fetch_scale"] == pytest.approx(cal["copy_bytes"] / (cal["fetch_kib"] * 1024), rel=1e-5)
+    assert cal["write_scale"] == pytest.approx(cal["copy_bytes"] / (cal["write_kib"] * 1024), rel=1e-5)
+    kib = rec["per_launch_kib"]
+    total = sum(v["FETCH_SIZE"] for v in kib.values()) * 1024 * cal["fetch_scale"] + \
+        sum(v["WRITE_SIZE"] for v in kib.values()) * 1024 * cal["write_scale"]
+    assert rec["traffic_bytes_per_launch"] == pytest.approx(total, rel=1e-6)
+    w = make_config(2)
+    alg = bench.decode_bytes(w)[0] + bench.store_bytes(w)
+    assert rec["algorithmic_bytes_per_launch"] == alg
+    assert 1.0 <= rec["traffic_bytes_per_launch"] / alg < 1.05
+    if rec["kernel_sources_sha256"] == bench.decode_sources_sha256():
+        assert bench.decode_traffic_bytes() == rec["traffic_bytes_per_launch"]
+    monkeypatch.setattr(bench, "decode_sources_sha256", lambda: "0" * 64)
+    assert bench.decode_traffic_bytes() is None
