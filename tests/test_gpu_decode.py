@@ -105,6 +105,31 @@ def test_decode_segment_of_more_than_64_pieces(case):
     assert_attention_close(ds.out_f64(), ref, atol=atol, rel_l2=l2, label=w.name)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(16, 8, 128), (16, 2, 64)])
+def test_decode_few_row_combine_is_bitwise_the_general_one(Hq, Hkv, D):
+    """Calls of at most 256 (sequence, q head) rows merge their partials with a combine that
+    loads more slots up front; it must give the same bits as the general combine. The same
+    16 sequences go through both: alone (256 rows) and with a 17th, empty sequence (272
+    rows); 256-key shares and the unchanged keys keep the split identical."""
+    ctx = [3000, 1, 2048, 4095, 700, 2500, 1500, 3999, 256, 257, 3100, 2222, 900, 4000, 1234,
+           2600, 5]
+    w = make_decode(230 + Hkv, ctx, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16", bs=256,
+                    name=f"few_rows_h{Hkv}")
+    ds = DeviceStep(w, partition_size=256)
+    ds.store()
+    ds.context_lens[16] = 0
+    ds.attend()                                   # 272 rows: the general combine
+    torch.cuda.synchronize()
+    general = ds.out[:16].clone()
+    few = torch.full_like(general, float("nan"))
+    B.paged_attn_decode(few, ds.q[:16], ds.k_cache, ds.v_cache, ds.block_tables[:16],
+                        ds.context_lens[:16], w.scale, workspace=ds.workspace,
+                        partition_size=256)       # 256 rows: the few-rows combine
+    torch.cuda.synchronize()
+    assert torch.equal(general.view(torch.int16), few.view(torch.int16))
+    assert bool(torch.isfinite(few.float()).all())
+
+
 def test_decode_peaked_logits():
     w = make_config(2, q_mult=4.0)
     check(w)
