@@ -28,6 +28,7 @@ _f = ctypes.c_float
 # name -> (restype, argtypes); the exact declarations of include/paged_kv.h
 SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [_c_int]),
+    "pkv_set_decode_kv_loads": (_c_int, [_i32]),
     "pkv_prefill_metadata": (_c_int, [_i32, _p, _p, _p, _p, _i32, _i32, _p, _p, _p, _p, _p, _i64,
                                       _p, _p]),
     "pkv_decode_metadata": (_c_int, [_i32, _p, _p, _p, _i32, _i32, _p, _p, _p, _p]),
@@ -207,6 +208,19 @@ def store_kvcache(key, value, k_cache, v_cache, slot_mapping, stream=None):
                                       _t_ptr(slot_mapping), N, Hkv, D, _dtype_code(key),
                                       _stream(stream))
     _check("store_kvcache", rc)
+
+
+PKV_KV_LOADS_CACHED = 0
+PKV_KV_LOADS_STREAM = 1
+
+
+def pkv_set_decode_kv_loads(policy: int) -> int:
+    """How decode calls read the cached K/V rows: PKV_KV_LOADS_CACHED (default) or
+    PKV_KV_LOADS_STREAM (non-temporal, for batches in which no block is read twice).
+    Process-wide; returns the previous policy."""
+    rc = load_library().pkv_set_decode_kv_loads(int(policy))
+    _check("pkv_set_decode_kv_loads", min(rc, 0))
+    return rc
 
 
 def paged_attn_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq,

@@ -4,6 +4,8 @@
 #include <stdlib.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include <hip/hip_runtime.h>
 
 #include "launch.hpp"
@@ -18,6 +20,9 @@ bool supported_group(int32_t heads, int32_t kv_heads) {
   return g == 1 || g == 2 || g == 4 || g == 8;
 }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// How decode calls read the cached K/V rows (pkv_set_decode_kv_loads); read at each launch.
+std::atomic<int32_t> g_decode_kv_loads{PKV_KV_LOADS_CACHED};
 
 // The attention kernels move rows in 16-byte vector accesses.
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -181,6 +186,11 @@ int store_kvcache(const void* key, int64_t key_token_stride, const void* value,
 }
 
 // ------------------------------------------------------------------------- decode
+int pkv_set_decode_kv_loads(int32_t policy) {
+  if (policy != PKV_KV_LOADS_CACHED && policy != PKV_KV_LOADS_STREAM) return PKV_ERR_INVALID;
+  return g_decode_kv_loads.exchange(policy);
+}
+
 size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                          int32_t max_blocks_per_seq, int32_t block_size,
                                          int32_t partition_size) {
@@ -275,6 +285,7 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
     const int v = atoi(env);
     if (v > 0) a.max_workgroups = v;
   }
+  a.stream_kv = g_decode_kv_loads.load(std::memory_order_relaxed) == PKV_KV_LOADS_STREAM;
   a.ws_ml = (float*)workspace + (size_t)num_seqs * num_heads * max_parts * head_dim;
   a.ws_meta = (int32_t*)(a.ws_ml + (size_t)num_seqs * num_heads * max_parts * 2);
   a.new_k = fused ? key : nullptr;  // the kernels key the fused path on new_k

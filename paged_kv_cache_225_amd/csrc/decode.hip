@@ -26,7 +26,10 @@
 // into its slot, and decode_combine_kernel merges the slots of each (sequence, head):
 //   M = max_p m_p, L = sum_p 2^(m_p - M) l_p, out = sum_p 2^(m_p - M) o_p / L.
 // Keys past the context length are never loaded, so block-table padding and the unused
-// (possibly NaN) slots of a sequence's last block are not touched.
+// (possibly NaN) slots of a sequence's last block are not touched. With NT the K/V rows
+// are read with non-temporal loads (the caller has said no block is read twice in the
+// call, so keeping the rows in the caches only displaces other lines); the arithmetic is
+// the same either way.
 //
 // Fused store (the store_kvcache that precedes decode attention in the engine's
 // Attention.forward): the stream kernel takes n_b - 1 keys of each sequence from the cache
@@ -58,7 +61,7 @@ struct Chunk {
   bool piece_start, piece_end;
 };
 
-template <typename T, int D, int G, int NI, int HPW>
+template <typename T, int D, int G, int NI, int HPW, bool NT>
 __global__ __launch_bounds__(256) void decode_stream_kernel(
     T* __restrict__ out, const T* __restrict__ q, const T* __restrict__ k_cache,
     const T* __restrict__ v_cache, int32_t num_blocks, const int32_t* __restrict__ block_tables,
@@ -177,8 +180,13 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
       if (r < c.cnt) {
         if ((unsigned)blk < (unsigned)num_blocks) {
           const int64_t off = (((int64_t)blk << bs_log2) + (j & bs_mask)) * row_elems + head_off;
-          kr[i] = load16(k_cache + off);
-          vr[i] = load16(v_cache + off);
+          if constexpr (NT) {
+            kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k_cache + off));
+            vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(v_cache + off));
+          } else {
+            kr[i] = load16(k_cache + off);
+            vr[i] = load16(v_cache + off);
+          }
         } else {
           kr[i] = E::nan_chunk();
           vr[i] = E::nan_chunk();
@@ -572,7 +580,9 @@ static int run_decode(const DecodeArgs& a, hipStream_t stream) {
   if (blocks > a.max_workgroups) blocks = a.max_workgroups;
   if (blocks < 1) blocks = 1;
   const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
-  hipLaunchKernelGGL((decode_stream_kernel<T, D, G, NI, HPW>), dim3((unsigned)blocks), dim3(256),
+  auto* stream_kernel = a.stream_kv ? decode_stream_kernel<T, D, G, NI, HPW, true>
+                                    : decode_stream_kernel<T, D, G, NI, HPW, false>;
+  hipLaunchKernelGGL(stream_kernel, dim3((unsigned)blocks), dim3(256),
                      lds, stream, (T*)a.out, (const T*)a.q, (const T*)a.k_cache,
                      (const T*)a.v_cache, a.num_blocks, a.block_tables, a.max_blocks_per_seq,
                      a.context_lens, a.num_seqs, a.num_kv_heads, bs_log2, c, a.partition,

@@ -297,3 +297,16 @@ def test_decode_traffic_record_is_consistent(monkeypatch):
         assert bench.decode_traffic_bytes() == rec["traffic_bytes_per_launch"]
     monkeypatch.setattr(bench, "decode_sources_sha256", lambda: "0" * 64)
     assert bench.decode_traffic_bytes() is None
+
+
+def test_decode_kv_loads_policy_setter():
+    # process-wide; returns the previous policy; any other value is rejected unchanged
+    prev = B.pkv_set_decode_kv_loads(B.PKV_KV_LOADS_STREAM)
+    try:
+        assert B.pkv_set_decode_kv_loads(B.PKV_KV_LOADS_CACHED) == B.PKV_KV_LOADS_STREAM
+        lib = B.load_library()
+        assert lib.pkv_set_decode_kv_loads(2) == -1
+        assert lib.pkv_set_decode_kv_loads(-1) == -1
+        assert lib.pkv_set_decode_kv_loads(B.PKV_KV_LOADS_CACHED) == B.PKV_KV_LOADS_CACHED
+    finally:
+        B.pkv_set_decode_kv_loads(prev)

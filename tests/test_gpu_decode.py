@@ -130,6 +130,31 @@ def test_decode_few_row_combine_is_bitwise_the_general_one(Hq, Hkv, D):
     assert bool(torch.isfinite(few.float()).all())
 
 
+@pytest.mark.parametrize("cfg,fused", [(2, False), (2, True), (1, False)])
+def test_decode_streaming_kv_loads_are_bitwise_the_cached_ones(cfg, fused):
+    """The K/V load policy changes only how the rows pass the caches: outputs and the cache
+    written by the fused store are bit for bit the same under both."""
+    w = make_config(cfg)
+    outs, pools = [], []
+    for policy in (B.PKV_KV_LOADS_CACHED, B.PKV_KV_LOADS_STREAM):
+        prev = B.pkv_set_decode_kv_loads(policy)
+        try:
+            ds = DeviceStep(w)
+            (ds.step_fused if fused else ds.step)()
+            torch.cuda.synchronize()
+        finally:
+            B.pkv_set_decode_kv_loads(prev)
+        outs.append(ds.out.clone())
+        pools.append((ds.k_cache.clone(), ds.v_cache.clone()))
+    bits = torch.int16 if w.dtype == "bf16" else torch.int32
+    assert torch.equal(outs[0].view(bits), outs[1].view(bits))
+    for a, b in zip(pools[0], pools[1]):
+        assert torch.equal(a.view(bits), b.view(bits))
+    ref, _, _, _ = run_workload(w)
+    atol, l2 = (1e-4, 1e-5) if w.dtype == "f32" else (2e-2, 1e-2)
+    assert_attention_close(ds.out_f64(), ref, atol=atol, rel_l2=l2, label=w.name)  # streaming run
+
+
 def test_decode_peaked_logits():
     w = make_config(2, q_mult=4.0)
     check(w)
