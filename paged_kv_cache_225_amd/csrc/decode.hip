@@ -632,9 +632,16 @@ static int run_decode_hpw(const DecodeArgs& a, hipStream_t s) {
 
 template <typename T, int D>
 static int dispatch_g(const DecodeArgs& a, hipStream_t s) {
+  // A call that fills the grid (every workgroup gets a share of at least the partition)
+  // keeps enough loads in flight with 4 load instructions per chunk, and the shorter chunk
+  // trims the tail; a small call has few workgroups and needs the deeper chunk. Measured
+  // with 2 q heads per kv head: batch 64 98.2 -> 96.4 us per call, batch 16 -2.5%, batch
+  // 512 unchanged, batch 1 and 4 6-7% slower with the shorter chunk.
+  const int64_t cap = (int64_t)a.max_blocks_per_seq * a.block_size;
+  const bool full = (int64_t)a.num_seqs * cap >= (int64_t)a.max_workgroups * a.partition;
   switch (a.num_heads / a.num_kv_heads) {
     case 1: return run_decode_hpw<T, D, 1, 8>(a, s);
-    case 2: return run_decode_hpw<T, D, 2, 8>(a, s);
+    case 2: return full ? run_decode_hpw<T, D, 2, 4>(a, s) : run_decode_hpw<T, D, 2, 8>(a, s);
     case 4: return run_decode_hpw<T, D, 4, 4>(a, s);
     case 8: return run_decode_hpw<T, D, 8, 2>(a, s);
     default: return -2;
