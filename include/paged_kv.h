@@ -63,7 +63,8 @@ const char* pkv_status_string(int status);
  *   block_tables[num_seqs * table_width]: each table copied and padded with -1.
  * Inputs: block tables are ragged, sequence b's ids are
  *   block_table_flat[block_table_offsets[b] .. block_table_offsets[b+1]-1].
- * slot_capacity / positions may be 0 / NULL to skip those outputs' size check / output.
+ * slot_capacity may be 0 to skip the check of slot_mapping's size (the caller vouches that it
+ * holds total_q entries); positions may be NULL to skip that output.
  * Errors: PKV_ERR_INVALID if a table holds fewer than ceil(end / bs) ids, if a table is
  * longer than table_width, if total_q exceeds slot_capacity, or on negative counts.
  * -------------------------------------------------------------------------------------*/
@@ -139,6 +140,8 @@ int store_kvcache(const void* key, int64_t key_token_stride,
  *                every call with fewer sequences), owned by the caller; no initial
  *                contents needed; in use until the stream passes the end of the call, so
  *                calls that overlap on different streams need different workspaces.
+ *   kv_stream_from  block-table column from which K/V rows are read with non-temporal
+ *                loads (see above); it changes no result.
  * out, q, k_cache, v_cache and workspace must be 16-byte aligned (PKV_ERR_INVALID otherwise).
  * Preconditions: num_blocks >= 1; n <= max_blocks_per_seq * bs (larger n is clamped to
  * that); table entries below ceil(n / bs) lie in [0, num_blocks) - an entry outside it is
@@ -151,24 +154,23 @@ size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, in
                                          int32_t max_blocks_per_seq, int32_t block_size,
                                          int32_t partition_size);
 
-/* How decode calls (paged_attn_decode, paged_attn_decode_store and the steps recorded by
- * pkv_decode_graphs_create) read the cached K/V rows. A tuning choice for the caller, who
- * knows from its block manager's reference counts whether the batch shares blocks (prefix
- * caching shares the leading blocks of sequences with a common prompt prefix):
- *   PKV_KV_LOADS_CACHED  ordinary loads (default): a block several sequences read, and a
- *                        small step's K/V read again next step, can be served from cache.
- *   PKV_KV_LOADS_STREAM  non-temporal loads, for batches in which no block is read twice:
- *                        the rows then stream past the caches without displacing other
- *                        lines. Measured on the batch-64 workload (non-overlapping tables,
- *                        4 layer pools rotated): 109.6 -> 98.1 us per call; on the batch-512
- *                        workload, where half the sequences share leading blocks, 310.6 ->
- *                        333.8 us, so that batch keeps the default.
- * Outputs are bitwise the same under both. The setting is process-wide, read when a call
- * launches (a recorded graph keeps the loads it was recorded with), and safe to change from
- * any thread between calls. Returns the previous policy, or PKV_ERR_INVALID for any other
- * value. */
-enum { PKV_KV_LOADS_CACHED = 0, PKV_KV_LOADS_STREAM = 1 };
-int pkv_set_decode_kv_loads(int32_t policy);
+/* kv_stream_from - how a decode call (paged_attn_decode, paged_attn_decode_store and the
+ * steps recorded by pkv_decode_graphs_create) reads the cached K/V rows; an argument of each
+ * call, so calls on different threads or streams never affect each other. Rows of block-table
+ * columns >= kv_stream_from are read with non-temporal loads, the others with ordinary loads.
+ * A tuning choice for the caller, who knows from its block manager which leading table
+ * columns may hold blocks that several sequences of the batch read (prefix caching shares
+ * only the leading full blocks of a table):
+ *   PKV_KV_STREAM_ALL (0)          no block is read twice in the call: every row streams past
+ *                                  the caches without displacing other lines. Measured on the
+ *                                  batch-64 workload (non-overlapping tables, 4 layer pools
+ *                                  rotated): 109.6 -> 98.1 us per call.
+ *   k (> 0)                        columns 0 .. k-1 may be shared: their re-reads can be served
+ *                                  from cache, the private rest streams.
+ *   PKV_KV_STREAM_NONE (INT32_MAX) ordinary loads for every row (a small step's K/V, read again
+ *                                  by the next step, can then stay cached).
+ * Outputs are bitwise the same for every value. Negative values are PKV_ERR_INVALID. */
+enum { PKV_KV_STREAM_ALL = 0, PKV_KV_STREAM_NONE = 0x7fffffff };
 
 int paged_attn_decode(void* out, const void* q,
                       const void* k_cache, const void* v_cache, int32_t num_blocks,
@@ -176,8 +178,8 @@ int paged_attn_decode(void* out, const void* q,
                       const int32_t* context_lens, int32_t num_seqs,
                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                       int32_t block_size, float scale, pkv_dtype_t dtype,
-                      int32_t partition_size, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream);
+                      int32_t partition_size, int32_t kv_stream_from,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Decode attention with the step's store fused in - [P1] Attention.forward, decode branch:
@@ -208,8 +210,8 @@ int paged_attn_decode_store(void* out, const void* q,
                             const int32_t* context_lens, int32_t num_seqs,
                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                             int32_t block_size, float scale, pkv_dtype_t dtype,
-                            int32_t partition_size, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream);
+                            int32_t partition_size, int32_t kv_stream_from,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Decode steps replayed from captured HIP graphs - [P1] ModelRunner.capture_cudagraph and
@@ -251,7 +253,8 @@ int pkv_decode_graphs_create(pkv_decode_graphs** handle, int32_t max_batch,
                              const int32_t* context_lens,
                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                              int32_t block_size, float scale, pkv_dtype_t dtype,
-                             int32_t partition_size, void* workspace, size_t workspace_bytes);
+                             int32_t partition_size, int32_t kv_stream_from,
+                             void* workspace, size_t workspace_bytes);
 int pkv_decode_graphs_count(const pkv_decode_graphs* handle);
 int pkv_decode_graphs_buckets(const pkv_decode_graphs* handle, int32_t* buckets,
                               int32_t capacity);

@@ -28,20 +28,19 @@ _f = ctypes.c_float
 # name -> (restype, argtypes); the exact declarations of include/paged_kv.h
 SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [_c_int]),
-    "pkv_set_decode_kv_loads": (_c_int, [_i32]),
     "pkv_prefill_metadata": (_c_int, [_i32, _p, _p, _p, _p, _i32, _i32, _p, _p, _p, _p, _p, _i64,
                                       _p, _p]),
     "pkv_decode_metadata": (_c_int, [_i32, _p, _p, _p, _i32, _i32, _p, _p, _p, _p]),
     "store_kvcache": (_c_int, [_p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _i32, _i32, _c_int, _p]),
     "paged_attn_decode_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "paged_attn_decode": (_c_int, [_p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32,
-                                   _i32, _f, _c_int, _i32, _p, _size, _p]),
+                                   _i32, _f, _c_int, _i32, _i32, _p, _size, _p]),
     "paged_attn_decode_store": (_c_int, [_p, _p, _p, _i64, _p, _i64, _p, _p, _p, _i32, _p, _i32,
-                                         _p, _i32, _i32, _i32, _i32, _i32, _f, _c_int, _i32, _p,
-                                         _size, _p]),
+                                         _p, _i32, _i32, _i32, _i32, _i32, _f, _c_int, _i32, _i32,
+                                         _p, _size, _p]),
     "pkv_decode_graphs_create": (_c_int, [ctypes.POINTER(_p), _i32, _p, _p, _p, _i64, _p, _i64,
                                           _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32,
-                                          _i32, _f, _c_int, _i32, _p, _size]),
+                                          _i32, _f, _c_int, _i32, _i32, _p, _size]),
     "pkv_decode_graphs_count": (_c_int, [_p]),
     "pkv_decode_graphs_buckets": (_c_int, [_p, _p, _i32]),
     "pkv_decode_graphs_bucket": (_c_int, [_p, _i32]),
@@ -210,17 +209,9 @@ def store_kvcache(key, value, k_cache, v_cache, slot_mapping, stream=None):
     _check("store_kvcache", rc)
 
 
-PKV_KV_LOADS_CACHED = 0
-PKV_KV_LOADS_STREAM = 1
-
-
-def pkv_set_decode_kv_loads(policy: int) -> int:
-    """How decode calls read the cached K/V rows: PKV_KV_LOADS_CACHED (default) or
-    PKV_KV_LOADS_STREAM (non-temporal, for batches in which no block is read twice).
-    Process-wide; returns the previous policy."""
-    rc = load_library().pkv_set_decode_kv_loads(int(policy))
-    _check("pkv_set_decode_kv_loads", min(rc, 0))
-    return rc
+# kv_stream_from: K/V rows of block-table columns >= this are read with non-temporal loads
+PKV_KV_STREAM_ALL = 0
+PKV_KV_STREAM_NONE = 0x7FFFFFFF
 
 
 def paged_attn_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq,
@@ -230,9 +221,11 @@ def paged_attn_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_
 
 
 def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                      workspace=None, partition_size=0, stream=None):
+                      workspace=None, partition_size=0, kv_stream_from=PKV_KV_STREAM_NONE,
+                      stream=None):
     """out/q [B, Hq, D]; caches [num_blocks, bs, Hkv, D]; block_tables int32 [B, W];
-    context_lens int32 [B]; workspace: a device tensor of at least the queried bytes."""
+    context_lens int32 [B]; workspace: a device tensor of at least the queried bytes;
+    kv_stream_from: first block-table column read with non-temporal loads."""
     B, Hq, D = q.shape
     num_blocks, bs, Hkv, _ = k_cache.shape
     W = block_tables.shape[1]
@@ -240,12 +233,14 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
     rc = load_library().paged_attn_decode(
         _t_ptr(out), _t_ptr(q), _t_ptr(k_cache), _t_ptr(v_cache), num_blocks,
         _t_ptr(block_tables), W, _t_ptr(context_lens), B, Hq, Hkv, D, bs, float(scale),
-        _dtype_code(q), partition_size, _t_ptr(workspace), ws_bytes, _stream(stream))
+        _dtype_code(q), partition_size, int(kv_stream_from), _t_ptr(workspace), ws_bytes,
+        _stream(stream))
     _check("paged_attn_decode", rc)
 
 
 def paged_attn_decode_store(out, q, key, value, slot_mapping, k_cache, v_cache, block_tables,
-                            context_lens, scale, workspace=None, partition_size=0, stream=None):
+                            context_lens, scale, workspace=None, partition_size=0,
+                            kv_stream_from=PKV_KV_STREAM_NONE, stream=None):
     """paged_attn_decode with the step's store fused in: key/value [B, Hkv, D] (token stride
     free, head stride D, unit element stride) are the newest tokens' rows, written to
     slot_mapping int32 [B]; other arguments as paged_attn_decode."""
@@ -259,7 +254,8 @@ def paged_attn_decode_store(out, q, key, value, slot_mapping, k_cache, v_cache, 
         _t_ptr(out), _t_ptr(q), _t_ptr(key), key.stride(0), _t_ptr(value), value.stride(0),
         _t_ptr(slot_mapping), _t_ptr(k_cache), _t_ptr(v_cache), num_blocks,
         _t_ptr(block_tables), W, _t_ptr(context_lens), B, Hq, Hkv, D, bs, float(scale),
-        _dtype_code(q), partition_size, _t_ptr(workspace), ws_bytes, _stream(stream))
+        _dtype_code(q), partition_size, int(kv_stream_from), _t_ptr(workspace), ws_bytes,
+        _stream(stream))
     _check("paged_attn_decode_store", rc)
 
 
@@ -303,7 +299,8 @@ class DecodeGraphs:
     context_lens 0 and slot_mapping -1 (``pad`` does that)."""
 
     def __init__(self, out, q, key, value, slot_mapping, k_cache, v_cache, block_tables,
-                 context_lens, scale, workspace, partition_size=0):
+                 context_lens, scale, workspace, partition_size=0,
+                 kv_stream_from=PKV_KV_STREAM_NONE):
         max_batch, Hq, D = q.shape
         num_blocks, bs, Hkv, _ = k_cache.shape
         if key.stride(2) != 1 or key.stride(1) != D or value.stride(2) != 1 or value.stride(1) != D:
@@ -318,7 +315,7 @@ class DecodeGraphs:
             _t_ptr(value), value.stride(0), _t_ptr(slot_mapping), _t_ptr(k_cache),
             _t_ptr(v_cache), num_blocks, _t_ptr(block_tables), block_tables.shape[1],
             _t_ptr(context_lens), Hq, Hkv, D, bs, float(scale), _dtype_code(q), partition_size,
-            _t_ptr(workspace), ws_bytes)
+            int(kv_stream_from), _t_ptr(workspace), ws_bytes)
         _check("pkv_decode_graphs_create", rc)
         self._h = h
         self.max_batch = max_batch

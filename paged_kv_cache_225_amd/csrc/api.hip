@@ -4,8 +4,6 @@
 #include <stdlib.h>
 #include <stdint.h>
 
-#include <atomic>
-
 #include <hip/hip_runtime.h>
 
 #include "launch.hpp"
@@ -21,8 +19,17 @@ bool supported_group(int32_t heads, int32_t kv_heads) {
 }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// How decode calls read the cached K/V rows (pkv_set_decode_kv_loads); read at each launch.
-std::atomic<int32_t> g_decode_kv_loads{PKV_KV_LOADS_CACHED};
+// Cap of the decode grid: PKV_DECODE_WORKGROUPS if set to a positive integer when the
+// library first launches a decode call, else the built-in default. Read once; a tuning knob
+// that changes how the keys are split, never what is computed.
+int32_t decode_workgroups() {
+  static const int32_t v = [] {
+    const char* env = getenv("PKV_DECODE_WORKGROUPS");
+    const int n = env ? atoi(env) : 0;
+    return n > 0 ? (int32_t)n : (int32_t)pkv::kDecodeDefaultWorkgroups;
+  }();
+  return v;
+}
 
 // The attention kernels move rows in 16-byte vector accesses.
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -98,7 +105,8 @@ int pkv_prefill_metadata(int32_t num_seqs, const int32_t* num_cached, const int3
       if (id < 0 || (id + 1) * (int64_t)block_size - 1 > INT32_MAX) return PKV_ERR_INVALID;
     }
   }
-  if (total_q > INT32_MAX || total_k > INT32_MAX || total_q > slot_capacity) return PKV_ERR_INVALID;
+  if (total_q > INT32_MAX || total_k > INT32_MAX) return PKV_ERR_INVALID;
+  if (slot_capacity > 0 && total_q > slot_capacity) return PKV_ERR_INVALID;  // 0: unchecked
   if (total_q > 0 && !slot_mapping) return PKV_ERR_INVALID;
   if (num_seqs > 0 && table_width > 0 && !block_tables) return PKV_ERR_INVALID;
 
@@ -186,11 +194,6 @@ int store_kvcache(const void* key, int64_t key_token_stride, const void* value,
 }
 
 // ------------------------------------------------------------------------- decode
-int pkv_set_decode_kv_loads(int32_t policy) {
-  if (policy != PKV_KV_LOADS_CACHED && policy != PKV_KV_LOADS_STREAM) return PKV_ERR_INVALID;
-  return g_decode_kv_loads.exchange(policy);
-}
-
 size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                          int32_t max_blocks_per_seq, int32_t block_size,
                                          int32_t partition_size) {
@@ -226,8 +229,8 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
                   int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
                   const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
-                  pkv_dtype_t dtype, int32_t partition_size, void* workspace,
-                  size_t workspace_bytes, bool fused, const void* key,
+                  pkv_dtype_t dtype, int32_t partition_size, int32_t kv_stream_from,
+                  void* workspace, size_t workspace_bytes, bool fused, const void* key,
                   int64_t key_token_stride, const void* value, int64_t value_token_stride,
                   const int32_t* slot_mapping, hipStream_t stream) {
   if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
@@ -236,6 +239,7 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
   if (!pow2_at_least_16(block_size)) return PKV_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (!supported_group(num_heads, num_kv_heads)) return PKV_ERR_UNSUPPORTED;
+  if (kv_stream_from < 0) return PKV_ERR_INVALID;
   if (num_seqs > 16383) return PKV_ERR_UNSUPPORTED;  // the context prefix lives in 64 KiB of LDS
   // the kernels number every key row of every (sequence, kv head) with an int32
   if ((int64_t)num_seqs * max_blocks_per_seq * block_size * num_kv_heads > INT32_MAX)
@@ -280,12 +284,9 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
   a.partition = part;
   a.max_parts = (int32_t)max_parts;
   a.ws_o = (float*)workspace;
-  a.max_workgroups = pkv::kDecodeDefaultWorkgroups;
-  if (const char* env = getenv("PKV_DECODE_WORKGROUPS")) {
-    const int v = atoi(env);
-    if (v > 0) a.max_workgroups = v;
-  }
-  a.stream_kv = g_decode_kv_loads.load(std::memory_order_relaxed) == PKV_KV_LOADS_STREAM;
+  a.max_workgroups = decode_workgroups();
+  // table columns at or past kv_stream_from are read with non-temporal loads
+  a.kv_stream_from = kv_stream_from < max_blocks_per_seq ? kv_stream_from : max_blocks_per_seq;
   a.ws_ml = (float*)workspace + (size_t)num_seqs * num_heads * max_parts * head_dim;
   a.ws_meta = (int32_t*)(a.ws_ml + (size_t)num_seqs * num_heads * max_parts * 2);
   a.new_k = fused ? key : nullptr;  // the kernels key the fused path on new_k
@@ -306,11 +307,12 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
                       int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
-                      pkv_dtype_t dtype, int32_t partition_size, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+                      pkv_dtype_t dtype, int32_t partition_size, int32_t kv_stream_from,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_common(out, q, k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                       scale, dtype, partition_size, workspace, workspace_bytes, false, nullptr,
+                       scale, dtype, partition_size, kv_stream_from, workspace, workspace_bytes,
+                       false, nullptr,
                        0, nullptr, 0, nullptr, stream);
 }
 
@@ -321,11 +323,12 @@ int paged_attn_decode_store(void* out, const void* q, const void* key, int64_t k
                             int32_t max_blocks_per_seq, const int32_t* context_lens,
                             int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t block_size, float scale, pkv_dtype_t dtype,
-                            int32_t partition_size, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream) {
+                            int32_t partition_size, int32_t kv_stream_from, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
   return decode_common(out, q, k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                       scale, dtype, partition_size, workspace, workspace_bytes, true, key,
+                       scale, dtype, partition_size, kv_stream_from, workspace, workspace_bytes,
+                       true, key,
                        key_token_stride, value, value_token_stride, slot_mapping, stream);
 }
 

@@ -26,10 +26,12 @@
 // into its slot, and decode_combine_kernel merges the slots of each (sequence, head):
 //   M = max_p m_p, L = sum_p 2^(m_p - M) l_p, out = sum_p 2^(m_p - M) o_p / L.
 // Keys past the context length are never loaded, so block-table padding and the unused
-// (possibly NaN) slots of a sequence's last block are not touched. With NT the K/V rows
-// are read with non-temporal loads (the caller has said no block is read twice in the
-// call, so keeping the rows in the caches only displaces other lines); the arithmetic is
-// the same either way.
+// (possibly NaN) slots of a sequence's last block are not touched. Rows of table columns
+// at or past the caller's kv_stream_from are read with non-temporal loads (the caller knows
+// that no block there is read twice in the call - prefix caching shares only the leading
+// blocks of a table - so keeping those rows in the caches would only displace other lines);
+// NT = 0: no column streamed, 1: every column, 2: decided per chunk. The arithmetic is the
+// same either way.
 //
 // Fused store (the store_kvcache that precedes decode attention in the engine's
 // Attention.forward): the stream kernel takes n_b - 1 keys of each sequence from the cache
@@ -61,14 +63,14 @@ struct Chunk {
   bool piece_start, piece_end;
 };
 
-template <typename T, int D, int G, int NI, int HPW, bool NT>
+template <typename T, int D, int G, int NI, int HPW, int NT>
 __global__ __launch_bounds__(256) void decode_stream_kernel(
     T* __restrict__ out, const T* __restrict__ q, const T* __restrict__ k_cache,
     const T* __restrict__ v_cache, int32_t num_blocks, const int32_t* __restrict__ block_tables,
     int32_t bt_stride, const int32_t* __restrict__ context_lens, int32_t num_seqs,
     int32_t num_kv_heads, int32_t bs_log2, float scale_log2e, int32_t min_keys,
     int32_t max_pieces, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-    int32_t* __restrict__ ws_meta, int32_t skip_last) {
+    int32_t* __restrict__ ws_meta, int32_t skip_last, int32_t kv_stream_from) {
   using E = Elem<T>;
   constexpr bool kBF16 = E::kBytes == 2;
   constexpr int EPL = E::kPerChunk;  // elements per 16-byte lane chunk
@@ -170,6 +172,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     // once from the window with a scalar lane read; otherwise each row shuffles its own
     const bool one_block = first == last;
     const int blk0 = __builtin_amdgcn_readlane(bt_reg, min(first - bt_base, 63));
+    const bool nt = NT == 1 || (NT == 2 && first >= kv_stream_from);  // wave-uniform
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = i * RPI + rsub;
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
       if (r < c.cnt) {
         if ((unsigned)blk < (unsigned)num_blocks) {
           const int64_t off = (((int64_t)blk << bs_log2) + (j & bs_mask)) * row_elems + head_off;
-          if constexpr (NT) {
+          if (nt) {
             kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k_cache + off));
             vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(v_cache + off));
           } else {
@@ -580,13 +583,16 @@ static int run_decode(const DecodeArgs& a, hipStream_t stream) {
   if (blocks > a.max_workgroups) blocks = a.max_workgroups;
   if (blocks < 1) blocks = 1;
   const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
-  auto* stream_kernel = a.stream_kv ? decode_stream_kernel<T, D, G, NI, HPW, true>
-                                    : decode_stream_kernel<T, D, G, NI, HPW, false>;
+  auto* stream_kernel = a.kv_stream_from >= a.max_blocks_per_seq
+                           ? decode_stream_kernel<T, D, G, NI, HPW, 0>
+                           : (a.kv_stream_from == 0 ? decode_stream_kernel<T, D, G, NI, HPW, 1>
+                                                    : decode_stream_kernel<T, D, G, NI, HPW, 2>);
   hipLaunchKernelGGL(stream_kernel, dim3((unsigned)blocks), dim3(256),
                      lds, stream, (T*)a.out, (const T*)a.q, (const T*)a.k_cache,
                      (const T*)a.v_cache, a.num_blocks, a.block_tables, a.max_blocks_per_seq,
                      a.context_lens, a.num_seqs, a.num_kv_heads, bs_log2, c, a.partition,
-                     a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, a.new_k != nullptr ? 1 : 0);
+                     a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, a.new_k != nullptr ? 1 : 0,
+                     a.kv_stream_from);
   const int rows = a.num_seqs * a.num_heads;
   NewTokens nt;
   nt.q = a.q;

@@ -74,7 +74,8 @@ int pkv_decode_graphs_create(pkv_decode_graphs** handle, int32_t max_batch,
                              const int32_t* context_lens,
                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                              int32_t block_size, float scale, pkv_dtype_t dtype,
-                             int32_t partition_size, void* workspace, size_t workspace_bytes) {
+                             int32_t partition_size, int32_t kv_stream_from, void* workspace,
+                             size_t workspace_bytes) {
   if (!handle) return PKV_ERR_INVALID;
   *handle = nullptr;
   if (max_batch < 1 || max_batch > 16383) return PKV_ERR_INVALID;
@@ -106,8 +107,8 @@ int pkv_decode_graphs_create(pkv_decode_graphs** handle, int32_t max_batch,
     const int call = paged_attn_decode_store(
         out, q, key, key_token_stride, value, value_token_stride, slot_mapping, k_cache,
         v_cache, num_blocks, block_tables, max_blocks_per_seq, context_lens, bs, num_heads,
-        num_kv_heads, head_dim, block_size, scale, dtype, partition_size, workspace,
-        workspace_bytes, cs);
+        num_kv_heads, head_dim, block_size, scale, dtype, partition_size, kv_stream_from,
+        workspace, workspace_bytes, cs);
     const hipError_t end = hipStreamEndCapture(cs, &graph);
     if (call != PKV_OK || end != hipSuccess || !graph) {
       if (graph) (void)hipGraphDestroy(graph);

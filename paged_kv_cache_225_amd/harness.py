@@ -38,10 +38,12 @@ def poison_fill_(t: torch.Tensor) -> torch.Tensor:
 
 
 class DeviceStep:
-    def __init__(self, w, device="cuda", fill=None, partition_size=0, table_width=None):
+    def __init__(self, w, device="cuda", fill=None, partition_size=0, table_width=None,
+                 kv_stream_from=B.PKV_KV_STREAM_NONE):
         self.w = w
         self.device = torch.device(device)
         self.partition_size = partition_size
+        self.kv_stream_from = kv_stream_from
         tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
         self.k_cache = torch.empty(shape, dtype=tdt, device=self.device)
@@ -117,7 +119,8 @@ class DeviceStep:
         if w.kind == "decode":
             B.paged_attn_decode(self.out, self.q, self.k_cache, self.v_cache, self.block_tables,
                                 self.context_lens, w.scale, workspace=self.workspace,
-                                partition_size=self.partition_size, stream=stream)
+                                partition_size=self.partition_size,
+                                kv_stream_from=self.kv_stream_from, stream=stream)
         else:
             B.paged_attn_prefill_varlen(self.out, self.q, self.k_cache, self.v_cache,
                                         self.block_tables, self.cu_seqlens_q, self.cu_seqlens_k,
@@ -135,7 +138,8 @@ class DeviceStep:
         B.paged_attn_decode_store(self.out, self.q, self.new_k, self.new_v, self.slot_mapping,
                                   self.k_cache, self.v_cache, self.block_tables,
                                   self.context_lens, w.scale, workspace=self.workspace,
-                                  partition_size=self.partition_size, stream=stream)
+                                  partition_size=self.partition_size,
+                                  kv_stream_from=self.kv_stream_from, stream=stream)
         return self.out
 
     def out_f64(self) -> np.ndarray:
@@ -149,7 +153,8 @@ class GraphDecodeStep:
     sequences' step inputs into the first rows and pads the rest of the bucket;
     ``launch(batch)`` replays the bucket's graph."""
 
-    def __init__(self, ds: DeviceStep, max_batch: int, width: int = None):
+    def __init__(self, ds: DeviceStep, max_batch: int, width: int = None,
+                 kv_stream_from=B.PKV_KV_STREAM_NONE):
         w = ds.w
         assert w.kind == "decode"
         self.ds = ds
@@ -171,7 +176,7 @@ class GraphDecodeStep:
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.graphs = B.DecodeGraphs(self.out, self.q, self.key, self.value, self.slots,
                                      ds.k_cache, ds.v_cache, self.tables, self.ctx, w.scale,
-                                     self.workspace, ds.partition_size)
+                                     self.workspace, ds.partition_size, kv_stream_from)
 
     def load(self, seqs):
         ds, n = self.ds, len(seqs)
@@ -188,7 +193,7 @@ class GraphDecodeStep:
         self.graphs.launch(batch, stream)
         return self.out[:batch]
 
-    def eager(self, batch, out=None, stream=None):
+    def eager(self, batch, out=None, stream=None, kv_stream_from=B.PKV_KV_STREAM_NONE):
         """The recorded call, made eagerly on the same padded buffers (bucket rows)."""
         n = self.graphs.bucket(batch)
         out = self.out if out is None else out
@@ -196,5 +201,6 @@ class GraphDecodeStep:
         B.paged_attn_decode_store(out[:n], self.q[:n], self.key[:n], self.value[:n],
                                   self.slots[:n], ds.k_cache, ds.v_cache, self.tables[:n],
                                   self.ctx[:n], ds.w.scale, workspace=self.workspace,
-                                  partition_size=ds.partition_size, stream=stream)
+                                  partition_size=ds.partition_size,
+                                  kv_stream_from=kv_stream_from, stream=stream)
         return out[:batch]

@@ -27,6 +27,9 @@ def assert_attention_close(gpu, ref, atol=ATOL, rtol=RTOL, rel_l2=None, label=""
     st = close_stats(gpu, ref)
     bad = np.abs(gpu - ref) > atol + rtol * np.abs(ref)
     assert not bad.any(), f"{label}: {int(bad.sum())} elements outside the gate; {st}"
+    # the max-abs half of the bar on its own (the elementwise form above lets an element
+    # with |ref| near 1 be off by atol + rtol)
+    assert st["max_abs"] <= atol, f"{label}: max-abs {st['max_abs']} > {atol}; {st}"
     if rel_l2 is not None:
         assert st["rel_l2"] <= rel_l2, f"{label}: rel-L2 {st['rel_l2']} > {rel_l2}; {st}"
     return st

@@ -118,23 +118,24 @@ FAKE = ctypes.c_void_p(0x1000)
 
 def _decode_rc(**kw):
     a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=16, bt=FAKE, W=4, ctx=FAKE, B=2, Hq=4, Hkv=2,
-             D=128, bs=256, scale=0.1, dt=B.PKV_BF16, part=0, ws=FAKE, ws_bytes=1 << 30)
+             D=128, bs=256, scale=0.1, dt=B.PKV_BF16, part=0, ksf=B.PKV_KV_STREAM_NONE, ws=FAKE,
+             ws_bytes=1 << 30)
     a.update(kw)
     return B.load_library().paged_attn_decode(a["out"], a["q"], a["k"], a["v"], a["nb"], a["bt"],
                                               a["W"], a["ctx"], a["B"], a["Hq"], a["Hkv"], a["D"],
-                                              a["bs"], a["scale"], a["dt"], a["part"], a["ws"],
-                                              a["ws_bytes"], None)
+                                              a["bs"], a["scale"], a["dt"], a["part"], a["ksf"],
+                                              a["ws"], a["ws_bytes"], None)
 
 
 def _decode_store_rc(**kw):
     a = dict(out=FAKE, q=FAKE, key=FAKE, ks=1024, value=FAKE, vs=1024, slots=FAKE, k=FAKE, v=FAKE,
              nb=16, bt=FAKE, W=4, ctx=FAKE, B=2, Hq=16, Hkv=8, D=128, bs=256, scale=0.1,
-             dt=B.PKV_BF16, part=0, ws=FAKE, ws_bytes=1 << 30)
+             dt=B.PKV_BF16, part=0, ksf=B.PKV_KV_STREAM_NONE, ws=FAKE, ws_bytes=1 << 30)
     a.update(kw)
     return B.load_library().paged_attn_decode_store(
         a["out"], a["q"], a["key"], a["ks"], a["value"], a["vs"], a["slots"], a["k"], a["v"],
         a["nb"], a["bt"], a["W"], a["ctx"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
-        a["scale"], a["dt"], a["part"], a["ws"], a["ws_bytes"], None)
+        a["scale"], a["dt"], a["part"], a["ksf"], a["ws"], a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -143,7 +144,7 @@ def _decode_store_rc(**kw):
     (dict(ks=1028), -1),                                  # 2056-byte stride: not 16-byte rows
     (dict(key=ctypes.c_void_p(0x1004)), -1), (dict(value=ctypes.c_void_p(0x1008)), -1),
     (dict(dt=7), -2), (dict(D=96), -2), (dict(ws_bytes=16), -3), (dict(B=0), 0),
-    (dict(B=0, key=None), 0),
+    (dict(B=0, key=None), 0), (dict(ksf=-1), -1),
 ])
 def test_decode_store_argument_validation(kw, status):
     assert _decode_store_rc(**kw) == status
@@ -163,7 +164,7 @@ def _prefill_rc(**kw):
     (dict(D=96), -2), (dict(Hq=6, Hkv=2), -2), (dict(Hq=5, Hkv=2), -1), (dict(bs=24), -2),
     (dict(bs=8), -2), (dict(dt=7), -2), (dict(part=100), -1), (dict(part=2048), -1),
     (dict(ws_bytes=16), -3), (dict(ws=None), -3), (dict(q=None), -1), (dict(B=0), 0),
-    (dict(W=0), -1), (dict(nb=0), -1),
+    (dict(W=0), -1), (dict(nb=0), -1), (dict(ksf=-1), -1), (dict(ksf=-5, B=0), -1),
     # 16-byte vector rows: misaligned out, q, caches or workspace are rejected
     (dict(out=ctypes.c_void_p(0x1002)), -1), (dict(q=ctypes.c_void_p(0x1008)), -1),
     (dict(k=ctypes.c_void_p(0x1004)), -1), (dict(v=ctypes.c_void_p(0x100c)), -1),
@@ -234,7 +235,7 @@ def test_decode_graphs_argument_validation():
     lib = B.load_library()
     h = ctypes.c_void_p()
     args = [FAKE, FAKE, FAKE, 1024, FAKE, 1024, FAKE, FAKE, FAKE, 16, FAKE, 16, FAKE,
-            16, 8, 128, 256, 0.1, B.PKV_BF16, 0]
+            16, 8, 128, 256, 0.1, B.PKV_BF16, 0, B.PKV_KV_STREAM_NONE]
     assert lib.pkv_decode_graphs_create(None, 4, *args, FAKE, 1 << 30) == -1
     assert lib.pkv_decode_graphs_create(ctypes.byref(h), 0, *args, FAKE, 1 << 30) == -1
     assert lib.pkv_decode_graphs_create(ctypes.byref(h), 16384, *args, FAKE, 1 << 30) == -1
@@ -299,14 +300,30 @@ def test_decode_traffic_record_is_consistent(monkeypatch):
     assert bench.decode_traffic_bytes() is None
 
 
-def test_decode_kv_loads_policy_setter():
-    # process-wide; returns the previous policy; any other value is rejected unchanged
-    prev = B.pkv_set_decode_kv_loads(B.PKV_KV_LOADS_STREAM)
-    try:
-        assert B.pkv_set_decode_kv_loads(B.PKV_KV_LOADS_CACHED) == B.PKV_KV_LOADS_STREAM
-        lib = B.load_library()
-        assert lib.pkv_set_decode_kv_loads(2) == -1
-        assert lib.pkv_set_decode_kv_loads(-1) == -1
-        assert lib.pkv_set_decode_kv_loads(B.PKV_KV_LOADS_CACHED) == B.PKV_KV_LOADS_CACHED
-    finally:
-        B.pkv_set_decode_kv_loads(prev)
+def test_decode_has_no_process_wide_setter():
+    # the K/V load choice is an argument of each decode call, not library state
+    assert not hasattr(B.load_library(), "pkv_set_decode_kv_loads")
+
+
+def test_prefill_metadata_slot_capacity_zero_skips_the_size_check():
+    # slot_capacity 0: the caller vouches for slot_mapping's size; a positive capacity below
+    # the step's token count is rejected before anything is written
+    lib = B.load_library()
+    cached = np.array([0], np.int32)
+    sched = np.array([3], np.int32)
+    flat = np.array([5], np.int32)
+    offs = np.array([0, 1], np.int64)
+    cu_q = np.zeros(2, np.int32)
+    cu_k = np.zeros(2, np.int32)
+    mq, mk = ctypes.c_int32(), ctypes.c_int32()
+    slots = np.full(3, -7, np.int32)
+    tables = np.zeros(1, np.int32)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    args = lambda cap: (1, p(cached), p(sched), p(flat), p(offs), 4, 1, p(cu_q), p(cu_k),
+                        ctypes.byref(mq), ctypes.byref(mk), p(slots), cap, None, p(tables))
+    assert lib.pkv_prefill_metadata(*args(2)) == -1
+    assert list(slots) == [-7, -7, -7]
+    assert lib.pkv_prefill_metadata(*args(0)) == 0
+    assert list(slots) == [20, 21, 22] and list(cu_q) == [0, 3] and mk.value == 3
+    assert lib.pkv_prefill_metadata(*args(3)) == 0
+    assert lib.pkv_prefill_metadata(*args(-1)) == -1

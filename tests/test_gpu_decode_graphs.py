@@ -120,18 +120,13 @@ def test_graph_decode_lengths_change_between_replays():
         assert_attention_close(st.out.double().cpu().numpy(), ref[seqs], label=f"rows {seqs}")
 
 
-def test_graph_recorded_with_streaming_loads_keeps_them():
-    """Graphs recorded while the decode K/V loads are set to streaming replay correctly after
-    the setting goes back to cached: the replay matches the oracle and equals, bit for bit,
-    the eager call made under either setting (the loads never change the arithmetic)."""
+def test_graph_recorded_with_streaming_loads():
+    """Graphs recorded with every K/V row streamed (kv_stream_from 0) replay correctly: the
+    replay matches the oracle and equals, bit for bit, the eager call made with either load
+    choice (the loads never change the arithmetic)."""
     w = make_config(2)
     ds = DeviceStep(w, table_width=W)
-    prev = B.pkv_set_decode_kv_loads(B.PKV_KV_LOADS_STREAM)
-    try:
-        st = GraphDecodeStep(ds, 64)
-    finally:
-        B.pkv_set_decode_kv_loads(prev)
-    assert B.pkv_set_decode_kv_loads(B.PKV_KV_LOADS_CACHED) == B.PKV_KV_LOADS_CACHED
+    st = GraphDecodeStep(ds, 64, kv_stream_from=B.PKV_KV_STREAM_ALL)
     ref, _, _, _ = run_workload(w)
     stream = torch.cuda.current_stream()
     seqs = np.random.Generator(np.random.PCG64(9)).choice(w.num_seqs, size=40, replace=False)
@@ -142,13 +137,9 @@ def test_graph_recorded_with_streaming_loads_keeps_them():
     torch.cuda.synchronize()
     assert_attention_close(st.out[:40].double().cpu().numpy(), ref[seqs], label="streaming graph")
     first = st.out[:bucket].clone()
-    for policy in (B.PKV_KV_LOADS_CACHED, B.PKV_KV_LOADS_STREAM):
-        prev = B.pkv_set_decode_kv_loads(policy)
-        try:
-            eager = torch.empty_like(st.out)
-            st.eager(40, out=eager, stream=stream)
-            torch.cuda.synchronize()
-        finally:
-            B.pkv_set_decode_kv_loads(prev)
-        assert torch.equal(_bits(eager[:bucket]), _bits(first)), policy
+    for ksf in (B.PKV_KV_STREAM_NONE, B.PKV_KV_STREAM_ALL):
+        eager = torch.empty_like(st.out)
+        st.eager(40, out=eager, stream=stream, kv_stream_from=ksf)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(eager[:bucket]), _bits(first)), ksf
     st.graphs.close()
