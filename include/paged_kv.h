@@ -182,6 +182,33 @@ int paged_attn_decode(void* out, const void* q,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * paged_attn_decode_noalloc - for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * operation and arguments as paged_attn_decode, without the workspace. The call allocates
+ * nothing; its split-K partials go to a library-owned device array of
+ * PKV_DECODE_NOALLOC_SCRATCH_BYTES, one per GPU, held from the library's first use on that
+ * GPU until the process ends (its address is looked up on the first call on each device).
+ * Results are bitwise those of paged_attn_decode with the same arguments.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents (no
+ * call needs it to start in any particular state): calls that overlap on one GPU - on
+ * different streams, or from different threads without ordering between their streams -
+ * race and may give wrong outputs. Calls on different GPUs never share it.
+ * Errors: as paged_attn_decode; PKV_ERR_WORKSPACE when the call would need more than
+ * PKV_DECODE_NOALLOC_SCRATCH_BYTES (paged_attn_decode_workspace_bytes with the same
+ * arguments reports the need; e.g. 9.1 MB for 64 sequences, 16 q heads, D 128 and
+ * 16 blocks of 256 keys per table); PKV_ERR_HIP if the array's address cannot be found.
+ * -------------------------------------------------------------------------------------*/
+#define PKV_DECODE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int paged_attn_decode_noalloc(void* out, const void* q,
+                              const void* k_cache, const void* v_cache, int32_t num_blocks,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, float scale, pkv_dtype_t dtype,
+                              int32_t partition_size, int32_t kv_stream_from,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * Decode attention with the step's store fused in - [P1] Attention.forward, decode branch:
  * store_kvcache of the step's K/V rows, then the decode attention over the cache.
  * Same result as store_kvcache(key, value, k_cache, v_cache, slot_mapping[0 .. num_seqs))

@@ -35,6 +35,8 @@ SIGNATURES = {
     "paged_attn_decode_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "paged_attn_decode": (_c_int, [_p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32,
                                    _i32, _f, _c_int, _i32, _i32, _p, _size, _p]),
+    "paged_attn_decode_noalloc": (_c_int, [_p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32,
+                                           _i32, _i32, _f, _c_int, _i32, _i32, _p]),
     "paged_attn_decode_store": (_c_int, [_p, _p, _p, _i64, _p, _i64, _p, _p, _p, _i32, _p, _i32,
                                          _p, _i32, _i32, _i32, _i32, _i32, _f, _c_int, _i32, _i32,
                                          _p, _size, _p]),
@@ -236,6 +238,23 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
         _dtype_code(q), partition_size, int(kv_stream_from), _t_ptr(workspace), ws_bytes,
         _stream(stream))
     _check("paged_attn_decode", rc)
+
+
+PKV_DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                              partition_size=0, kv_stream_from=PKV_KV_STREAM_NONE, stream=None):
+    """paged_attn_decode without a workspace: the library's per-GPU scratch array holds the
+    partials (calls that overlap on one GPU race)."""
+    B, Hq, D = q.shape
+    num_blocks, bs, Hkv, _ = k_cache.shape
+    W = block_tables.shape[1]
+    rc = load_library().paged_attn_decode_noalloc(
+        _t_ptr(out), _t_ptr(q), _t_ptr(k_cache), _t_ptr(v_cache), num_blocks,
+        _t_ptr(block_tables), W, _t_ptr(context_lens), B, Hq, Hkv, D, bs, float(scale),
+        _dtype_code(q), partition_size, int(kv_stream_from), _stream(stream))
+    _check("paged_attn_decode_noalloc", rc)
 
 
 def paged_attn_decode_store(out, q, key, value, slot_mapping, k_cache, v_cache, block_tables,

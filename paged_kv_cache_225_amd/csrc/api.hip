@@ -4,12 +4,51 @@
 #include <stdlib.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "launch.hpp"
 #include "paged_kv.h"
 
+// The decode workspace of paged_attn_decode_noalloc: device memory that the library owns, so
+// that a caller who cannot allocate (graph capture, a serving loop that forbids allocation)
+// passes inputs and outputs only. Each GPU the library runs on holds its own copy of the
+// array from module load until the process ends. Host code never passes `scratch` itself
+// (on the host its name stands for a host-side shadow, not a device address): it asks the
+// runtime for the device address once per device and passes that.
+static __device__ __align__(256) char scratch[PKV_DECODE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxScratchDevices = 256;
+std::atomic<void*> g_scratch_addr[kMaxScratchDevices];  // device address of `scratch`, per device
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the current device, looked up on the first call on that
+// device (with it current) and kept for the process.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+    (void)hipGetLastError();
+    return PKV_ERR_HIP;
+  }
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return PKV_ERR_HIP;
+      }
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PKV_OK;
+}
 
 bool pow2_at_least_16(int32_t v) { return v >= 16 && (v & (v - 1)) == 0; }
 bool supported_group(int32_t heads, int32_t kv_heads) {
@@ -330,6 +369,29 @@ int paged_attn_decode_store(void* out, const void* q, const void* key, int64_t k
                        scale, dtype, partition_size, kv_stream_from, workspace, workspace_bytes,
                        true, key,
                        key_token_stride, value, value_token_stride, slot_mapping, stream);
+}
+
+int paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              int32_t num_blocks, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, float scale, pkv_dtype_t dtype,
+                              int32_t partition_size, int32_t kv_stream_from, hipStream_t stream) {
+  // the bytes the call needs (0 when the arguments are invalid: decode_common reports why)
+  const size_t need = num_seqs > 0 ? paged_attn_decode_workspace_bytes(
+                                         num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                                         block_size, partition_size)
+                                   : 0;
+  if (need > (size_t)PKV_DECODE_NOALLOC_SCRATCH_BYTES) return PKV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int rc = scratch_on_current_device(&ws);
+    if (rc != PKV_OK) return rc;
+  }
+  return decode_common(out, q, k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       scale, dtype, partition_size, kv_stream_from, ws, need, false, nullptr, 0,
+                       nullptr, 0, nullptr, stream);
 }
 
 // ------------------------------------------------------------------------- prefill
