@@ -106,8 +106,9 @@ def bench_decode_headline(torch, args):
     from paged_kv_cache_225_amd import _binding as B
 
     # the workload's block tables do not overlap (no block is read twice in a step), so the
-    # caller streams every K/V row past the caches
-    ksf = B.PKV_KV_STREAM_ALL
+    # caller streams every K/V row past the caches (first streamed table column 0 for every
+    # sequence)
+    ksf = torch.zeros(w.num_seqs, dtype=torch.int32, device="cuda")
 
     def fused(i):
         kc, vc = layers[i % len(layers)]
@@ -212,14 +213,13 @@ def bench_prefill_packed(torch, iters, warmup, flush=None):
 
 
 def bench_large_decode(torch, iters, warmup, flush=None):
-    """The 512-sequence decode workload. Its block tables share up to 8 leading blocks (a
-    common prompt prefix); the caller, which knows that from its block manager, streams the
-    K/V rows of the table columns past them and keeps ordinary loads for the shared ones."""
+    """The 512-sequence decode workload. Half its sequences share 2-8 leading blocks (a
+    common prompt prefix); the caller, which knows each table's shared leading blocks from
+    its block manager, keeps ordinary loads for those and streams every other K/V row."""
     from paged_kv_cache_225_amd.harness import DeviceStep
     from workloads import CONFIG_NAMES, make_config
     w = make_config(5)
-    ksf = int(w.shared_blocks.max())
-    ds = DeviceStep(w, kv_stream_from=ksf)
+    ds = DeviceStep(w, kv_stream_from="shared")
     stream = torch.cuda.current_stream()
     ds.store(stream)
     med, p10, p90 = _median_event_ms(torch, lambda: ds.attend(stream), iters, warmup, stream,
@@ -231,7 +231,7 @@ def bench_large_decode(torch, iters, warmup, flush=None):
             "unique_gbs": uniq / (med * 1e-3) / 1e9, "logical_gbs": logi / (med * 1e-3) / 1e9,
             "frac_hbm_unique": uniq / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "tokens_per_s": w.num_seqs / (med * 1e-3), "shared_hist": w.meta.get("shared_hist"),
-            "kv_stream_from": ksf}
+            "kv_stream_from": "per sequence: its count of shared leading blocks"}
 
 
 def bench_tiny_decode(torch, iters, warmup, flush=None):
@@ -484,7 +484,7 @@ def main():
                    "head_dim": 128, "block_size": 256, "pool_blocks": 2048,
                    "context": "uniform[256,4096]", "layer_pools_rotated": args.layers,
                    "step": "paged_attn_decode_store: store of the 64 new tokens' K/V + decode attention, one call",
-                   "kv_stream_from": "0 (every K/V row non-temporal; the tables do not overlap)"},
+                   "kv_stream_from": "0 for every sequence (every K/V row non-temporal; the tables do not overlap)"},
         "roofline": head["roofline"],
         "tokens_per_s": head["tokens_per_s"],
         "decode_call_us_avg": head["decode_call_us_avg"],

@@ -140,8 +140,9 @@ int store_kvcache(const void* key, int64_t key_token_stride,
  *                every call with fewer sequences), owned by the caller; no initial
  *                contents needed; in use until the stream passes the end of the call, so
  *                calls that overlap on different streams need different workspaces.
- *   kv_stream_from  block-table column from which K/V rows are read with non-temporal
- *                loads (see above); it changes no result.
+ *   kv_stream_from  NULL or device int32 [num_seqs]: per sequence, the first block-table
+ *                column whose K/V rows are read with non-temporal loads (see below); it
+ *                changes no result.
  * out, q, k_cache, v_cache and workspace must be 16-byte aligned (PKV_ERR_INVALID otherwise).
  * Preconditions: num_blocks >= 1; n <= max_blocks_per_seq * bs (larger n is clamped to
  * that); table entries below ceil(n / bs) lie in [0, num_blocks) - an entry outside it is
@@ -154,23 +155,21 @@ size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, in
                                          int32_t max_blocks_per_seq, int32_t block_size,
                                          int32_t partition_size);
 
-/* kv_stream_from - how a decode call (paged_attn_decode, paged_attn_decode_store and the
- * steps recorded by pkv_decode_graphs_create) reads the cached K/V rows; an argument of each
- * call, so calls on different threads or streams never affect each other. Rows of block-table
- * columns >= kv_stream_from are read with non-temporal loads, the others with ordinary loads.
- * A tuning choice for the caller, who knows from its block manager which leading table
- * columns may hold blocks that several sequences of the batch read (prefix caching shares
- * only the leading full blocks of a table):
- *   PKV_KV_STREAM_ALL (0)          no block is read twice in the call: every row streams past
- *                                  the caches without displacing other lines. Measured on the
- *                                  batch-64 workload (non-overlapping tables, 4 layer pools
- *                                  rotated): 109.6 -> 98.1 us per call.
- *   k (> 0)                        columns 0 .. k-1 may be shared: their re-reads can be served
- *                                  from cache, the private rest streams.
- *   PKV_KV_STREAM_NONE (INT32_MAX) ordinary loads for every row (a small step's K/V, read again
- *                                  by the next step, can then stay cached).
- * Outputs are bitwise the same for every value. Negative values are PKV_ERR_INVALID. */
-enum { PKV_KV_STREAM_ALL = 0, PKV_KV_STREAM_NONE = 0x7fffffff };
+/* kv_stream_from - how a decode call (paged_attn_decode, paged_attn_decode_store,
+ * paged_attn_decode_noalloc and the steps recorded by pkv_decode_graphs_create) reads the
+ * cached K/V rows; an argument of each call, so calls on different threads or streams never
+ * affect each other. NULL: every row with ordinary loads. Otherwise a device int32 array
+ * [num_seqs]: sequence b's rows of block-table columns >= kv_stream_from[b] are read with
+ * non-temporal loads (they stream past the caches without displacing other lines), the
+ * others with ordinary loads. A tuning choice for the caller, who knows from its block
+ * manager's reference counts which leading blocks of each table other sequences of the batch
+ * also read (prefix caching shares only leading full blocks): pass each sequence's count of
+ * shared leading blocks - 0 when no block of the batch is read twice - so that the shared
+ * blocks stay cached for their other readers while the private rows stream. Measured on the
+ * batch-64 workload (non-overlapping tables, all 0, 4 layer pools rotated): 109.6 -> 98.1 us
+ * per call. Any value (negative: all streamed; >= the table width: none) is valid, and the
+ * outputs are bitwise the same for every choice. The array is read at run time, like
+ * context_lens, so a recorded graph follows its contents. */
 
 int paged_attn_decode(void* out, const void* q,
                       const void* k_cache, const void* v_cache, int32_t num_blocks,
@@ -178,7 +177,7 @@ int paged_attn_decode(void* out, const void* q,
                       const int32_t* context_lens, int32_t num_seqs,
                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                       int32_t block_size, float scale, pkv_dtype_t dtype,
-                      int32_t partition_size, int32_t kv_stream_from,
+                      int32_t partition_size, const int32_t* kv_stream_from,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
@@ -205,7 +204,7 @@ int paged_attn_decode_noalloc(void* out, const void* q,
                               const int32_t* context_lens, int32_t num_seqs,
                               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                               int32_t block_size, float scale, pkv_dtype_t dtype,
-                              int32_t partition_size, int32_t kv_stream_from,
+                              int32_t partition_size, const int32_t* kv_stream_from,
                               hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
@@ -237,7 +236,7 @@ int paged_attn_decode_store(void* out, const void* q,
                             const int32_t* context_lens, int32_t num_seqs,
                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                             int32_t block_size, float scale, pkv_dtype_t dtype,
-                            int32_t partition_size, int32_t kv_stream_from,
+                            int32_t partition_size, const int32_t* kv_stream_from,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
@@ -280,7 +279,7 @@ int pkv_decode_graphs_create(pkv_decode_graphs** handle, int32_t max_batch,
                              const int32_t* context_lens,
                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                              int32_t block_size, float scale, pkv_dtype_t dtype,
-                             int32_t partition_size, int32_t kv_stream_from,
+                             int32_t partition_size, const int32_t* kv_stream_from,
                              void* workspace, size_t workspace_bytes);
 int pkv_decode_graphs_count(const pkv_decode_graphs* handle);
 int pkv_decode_graphs_buckets(const pkv_decode_graphs* handle, int32_t* buckets,

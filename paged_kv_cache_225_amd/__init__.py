@@ -6,14 +6,13 @@ include/paged_kv.h). This package is the thin Python binding over it.
 from ._binding import (  # noqa: F401
     PKV_BF16,
     PKV_F32,
-    PKV_KV_STREAM_ALL,
-    PKV_KV_STREAM_NONE,
     BlockManager,
     DecodeGraphs,
     PagedKVError,
     attn_prefill_varlen,
     load_library,
     paged_attn_decode,
+    paged_attn_decode_noalloc,
     paged_attn_decode_store,
     paged_attn_decode_workspace_bytes,
     paged_attn_prefill_varlen,
@@ -28,8 +27,8 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "PKV_BF16", "PKV_F32", "PKV_KV_STREAM_ALL", "PKV_KV_STREAM_NONE", "BlockManager", "DecodeGraphs", "PagedKVError", "attn_prefill_varlen",
-    "load_library", "paged_attn_decode", "paged_attn_decode_store",
+    "PKV_BF16", "PKV_F32", "BlockManager", "DecodeGraphs", "PagedKVError", "attn_prefill_varlen",
+    "load_library", "paged_attn_decode", "paged_attn_decode_noalloc", "paged_attn_decode_store",
     "paged_attn_decode_workspace_bytes", "paged_attn_prefill_varlen", "pkv_decode_metadata",
     "pkv_block_hash", "pkv_prefill_metadata", "pkv_sample", "pkv_sample_workspace_bytes",
     "pkv_status_string", "pkv_xxh64", "store_kvcache",

@@ -34,15 +34,15 @@ SIGNATURES = {
     "store_kvcache": (_c_int, [_p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _i32, _i32, _c_int, _p]),
     "paged_attn_decode_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "paged_attn_decode": (_c_int, [_p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32,
-                                   _i32, _f, _c_int, _i32, _i32, _p, _size, _p]),
+                                   _i32, _f, _c_int, _i32, _p, _p, _size, _p]),
     "paged_attn_decode_noalloc": (_c_int, [_p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32,
-                                           _i32, _i32, _f, _c_int, _i32, _i32, _p]),
+                                           _i32, _i32, _f, _c_int, _i32, _p, _p]),
     "paged_attn_decode_store": (_c_int, [_p, _p, _p, _i64, _p, _i64, _p, _p, _p, _i32, _p, _i32,
-                                         _p, _i32, _i32, _i32, _i32, _i32, _f, _c_int, _i32, _i32,
+                                         _p, _i32, _i32, _i32, _i32, _i32, _f, _c_int, _i32, _p,
                                          _p, _size, _p]),
     "pkv_decode_graphs_create": (_c_int, [ctypes.POINTER(_p), _i32, _p, _p, _p, _i64, _p, _i64,
                                           _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32,
-                                          _i32, _f, _c_int, _i32, _i32, _p, _size]),
+                                          _i32, _f, _c_int, _i32, _p, _p, _size]),
     "pkv_decode_graphs_count": (_c_int, [_p]),
     "pkv_decode_graphs_buckets": (_c_int, [_p, _p, _i32]),
     "pkv_decode_graphs_bucket": (_c_int, [_p, _i32]),
@@ -211,10 +211,6 @@ def store_kvcache(key, value, k_cache, v_cache, slot_mapping, stream=None):
     _check("store_kvcache", rc)
 
 
-# kv_stream_from: K/V rows of block-table columns >= this are read with non-temporal loads
-PKV_KV_STREAM_ALL = 0
-PKV_KV_STREAM_NONE = 0x7FFFFFFF
-
 
 def paged_attn_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq,
                                       block_size, partition_size=0):
@@ -223,11 +219,12 @@ def paged_attn_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_
 
 
 def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                      workspace=None, partition_size=0, kv_stream_from=PKV_KV_STREAM_NONE,
+                      workspace=None, partition_size=0, kv_stream_from=None,
                       stream=None):
     """out/q [B, Hq, D]; caches [num_blocks, bs, Hkv, D]; block_tables int32 [B, W];
     context_lens int32 [B]; workspace: a device tensor of at least the queried bytes;
-    kv_stream_from: first block-table column read with non-temporal loads."""
+    kv_stream_from: None or a device int32 [B] tensor, per sequence the first block-table
+    column whose K/V rows are read with non-temporal loads."""
     B, Hq, D = q.shape
     num_blocks, bs, Hkv, _ = k_cache.shape
     W = block_tables.shape[1]
@@ -235,7 +232,7 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
     rc = load_library().paged_attn_decode(
         _t_ptr(out), _t_ptr(q), _t_ptr(k_cache), _t_ptr(v_cache), num_blocks,
         _t_ptr(block_tables), W, _t_ptr(context_lens), B, Hq, Hkv, D, bs, float(scale),
-        _dtype_code(q), partition_size, int(kv_stream_from), _t_ptr(workspace), ws_bytes,
+        _dtype_code(q), partition_size, _t_ptr(kv_stream_from), _t_ptr(workspace), ws_bytes,
         _stream(stream))
     _check("paged_attn_decode", rc)
 
@@ -244,7 +241,7 @@ PKV_DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                              partition_size=0, kv_stream_from=PKV_KV_STREAM_NONE, stream=None):
+                              partition_size=0, kv_stream_from=None, stream=None):
     """paged_attn_decode without a workspace: the library's per-GPU scratch array holds the
     partials (calls that overlap on one GPU race)."""
     B, Hq, D = q.shape
@@ -253,13 +250,13 @@ def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_le
     rc = load_library().paged_attn_decode_noalloc(
         _t_ptr(out), _t_ptr(q), _t_ptr(k_cache), _t_ptr(v_cache), num_blocks,
         _t_ptr(block_tables), W, _t_ptr(context_lens), B, Hq, Hkv, D, bs, float(scale),
-        _dtype_code(q), partition_size, int(kv_stream_from), _stream(stream))
+        _dtype_code(q), partition_size, _t_ptr(kv_stream_from), _stream(stream))
     _check("paged_attn_decode_noalloc", rc)
 
 
 def paged_attn_decode_store(out, q, key, value, slot_mapping, k_cache, v_cache, block_tables,
                             context_lens, scale, workspace=None, partition_size=0,
-                            kv_stream_from=PKV_KV_STREAM_NONE, stream=None):
+                            kv_stream_from=None, stream=None):
     """paged_attn_decode with the step's store fused in: key/value [B, Hkv, D] (token stride
     free, head stride D, unit element stride) are the newest tokens' rows, written to
     slot_mapping int32 [B]; other arguments as paged_attn_decode."""
@@ -273,7 +270,7 @@ def paged_attn_decode_store(out, q, key, value, slot_mapping, k_cache, v_cache, 
         _t_ptr(out), _t_ptr(q), _t_ptr(key), key.stride(0), _t_ptr(value), value.stride(0),
         _t_ptr(slot_mapping), _t_ptr(k_cache), _t_ptr(v_cache), num_blocks,
         _t_ptr(block_tables), W, _t_ptr(context_lens), B, Hq, Hkv, D, bs, float(scale),
-        _dtype_code(q), partition_size, int(kv_stream_from), _t_ptr(workspace), ws_bytes,
+        _dtype_code(q), partition_size, _t_ptr(kv_stream_from), _t_ptr(workspace), ws_bytes,
         _stream(stream))
     _check("paged_attn_decode_store", rc)
 
@@ -319,7 +316,7 @@ class DecodeGraphs:
 
     def __init__(self, out, q, key, value, slot_mapping, k_cache, v_cache, block_tables,
                  context_lens, scale, workspace, partition_size=0,
-                 kv_stream_from=PKV_KV_STREAM_NONE):
+                 kv_stream_from=None):
         max_batch, Hq, D = q.shape
         num_blocks, bs, Hkv, _ = k_cache.shape
         if key.stride(2) != 1 or key.stride(1) != D or value.stride(2) != 1 or value.stride(1) != D:
@@ -334,7 +331,7 @@ class DecodeGraphs:
             _t_ptr(value), value.stride(0), _t_ptr(slot_mapping), _t_ptr(k_cache),
             _t_ptr(v_cache), num_blocks, _t_ptr(block_tables), block_tables.shape[1],
             _t_ptr(context_lens), Hq, Hkv, D, bs, float(scale), _dtype_code(q), partition_size,
-            int(kv_stream_from), _t_ptr(workspace), ws_bytes)
+            _t_ptr(kv_stream_from), _t_ptr(workspace), ws_bytes)
         _check("pkv_decode_graphs_create", rc)
         self._h = h
         self.max_batch = max_batch

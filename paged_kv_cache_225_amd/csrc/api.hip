@@ -268,7 +268,7 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
                   int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
                   const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
-                  pkv_dtype_t dtype, int32_t partition_size, int32_t kv_stream_from,
+                  pkv_dtype_t dtype, int32_t partition_size, const int32_t* kv_stream_from,
                   void* workspace, size_t workspace_bytes, bool fused, const void* key,
                   int64_t key_token_stride, const void* value, int64_t value_token_stride,
                   const int32_t* slot_mapping, hipStream_t stream) {
@@ -278,7 +278,6 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
   if (!pow2_at_least_16(block_size)) return PKV_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (!supported_group(num_heads, num_kv_heads)) return PKV_ERR_UNSUPPORTED;
-  if (kv_stream_from < 0) return PKV_ERR_INVALID;
   if (num_seqs > 16383) return PKV_ERR_UNSUPPORTED;  // the context prefix lives in 64 KiB of LDS
   // the kernels number every key row of every (sequence, kv head) with an int32
   if ((int64_t)num_seqs * max_blocks_per_seq * block_size * num_kv_heads > INT32_MAX)
@@ -324,8 +323,7 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
   a.max_parts = (int32_t)max_parts;
   a.ws_o = (float*)workspace;
   a.max_workgroups = decode_workgroups();
-  // table columns at or past kv_stream_from are read with non-temporal loads
-  a.kv_stream_from = kv_stream_from < max_blocks_per_seq ? kv_stream_from : max_blocks_per_seq;
+  a.kv_stream_from = kv_stream_from;  // device [num_seqs] or null
   a.ws_ml = (float*)workspace + (size_t)num_seqs * num_heads * max_parts * head_dim;
   a.ws_meta = (int32_t*)(a.ws_ml + (size_t)num_seqs * num_heads * max_parts * 2);
   a.new_k = fused ? key : nullptr;  // the kernels key the fused path on new_k
@@ -346,8 +344,9 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
                       int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
-                      pkv_dtype_t dtype, int32_t partition_size, int32_t kv_stream_from,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      pkv_dtype_t dtype, int32_t partition_size,
+                      const int32_t* kv_stream_from, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
   return decode_common(out, q, k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                        scale, dtype, partition_size, kv_stream_from, workspace, workspace_bytes,
@@ -362,8 +361,8 @@ int paged_attn_decode_store(void* out, const void* q, const void* key, int64_t k
                             int32_t max_blocks_per_seq, const int32_t* context_lens,
                             int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t block_size, float scale, pkv_dtype_t dtype,
-                            int32_t partition_size, int32_t kv_stream_from, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
+                            int32_t partition_size, const int32_t* kv_stream_from,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_common(out, q, k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                        scale, dtype, partition_size, kv_stream_from, workspace, workspace_bytes,
@@ -376,7 +375,8 @@ int paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, con
                               int32_t max_blocks_per_seq, const int32_t* context_lens,
                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t block_size, float scale, pkv_dtype_t dtype,
-                              int32_t partition_size, int32_t kv_stream_from, hipStream_t stream) {
+                              int32_t partition_size, const int32_t* kv_stream_from,
+                              hipStream_t stream) {
   // the bytes the call needs (0 when the arguments are invalid: decode_common reports why)
   const size_t need = num_seqs > 0 ? paged_attn_decode_workspace_bytes(
                                          num_seqs, num_heads, head_dim, max_blocks_per_seq,

@@ -26,12 +26,12 @@
 // into its slot, and decode_combine_kernel merges the slots of each (sequence, head):
 //   M = max_p m_p, L = sum_p 2^(m_p - M) l_p, out = sum_p 2^(m_p - M) o_p / L.
 // Keys past the context length are never loaded, so block-table padding and the unused
-// (possibly NaN) slots of a sequence's last block are not touched. Rows of table columns
-// at or past the caller's kv_stream_from are read with non-temporal loads (the caller knows
-// that no block there is read twice in the call - prefix caching shares only the leading
-// blocks of a table - so keeping those rows in the caches would only displace other lines);
-// NT = 0: no column streamed, 1: every column, 2: decided per chunk. The arithmetic is the
-// same either way.
+// (possibly NaN) slots of a sequence's last block are not touched. When the caller passes
+// kv_stream_from (NT), sequence b's rows of table columns >= kv_stream_from[b] are read with
+// non-temporal loads: the caller knows from its block manager that no other sequence of the
+// call reads those blocks (prefix caching shares only leading blocks of a table), so keeping
+// their rows in the caches would only displace lines that are read again - the shared
+// leading blocks among them. The arithmetic is the same either way.
 //
 // Fused store (the store_kvcache that precedes decode attention in the engine's
 // Attention.forward): the stream kernel takes n_b - 1 keys of each sequence from the cache
@@ -40,6 +40,8 @@
 // first wavefront of each kv head copies those rows into their slots. No kernel of the call
 // reads the newest token's slot, so the copy needs no ordering against the attention.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -63,14 +65,15 @@ struct Chunk {
   bool piece_start, piece_end;
 };
 
-template <typename T, int D, int G, int NI, int HPW, int NT>
+template <typename T, int D, int G, int NI, int HPW, bool NT>
 __global__ __launch_bounds__(256) void decode_stream_kernel(
     T* __restrict__ out, const T* __restrict__ q, const T* __restrict__ k_cache,
     const T* __restrict__ v_cache, int32_t num_blocks, const int32_t* __restrict__ block_tables,
     int32_t bt_stride, const int32_t* __restrict__ context_lens, int32_t num_seqs,
     int32_t num_kv_heads, int32_t bs_log2, float scale_log2e, int32_t min_keys,
     int32_t max_pieces, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-    int32_t* __restrict__ ws_meta, int32_t skip_last, int32_t kv_stream_from) {
+    int32_t* __restrict__ ws_meta, int32_t skip_last,
+    const int32_t* __restrict__ kv_stream_from) {
   using E = Elem<T>;
   constexpr bool kBF16 = E::kBytes == 2;
   constexpr int EPL = E::kPerChunk;  // elements per 16-byte lane chunk
@@ -160,9 +163,13 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   // head of the sequence uses the same table, so the window is reloaded only when the
   // sequence changes or a chunk runs past it.
   int bt_b = -1, bt_base = 0, bt_reg = -1;
+  int stream_from = INT32_MAX;  // first table column of sequence bt_b read non-temporally
   auto issue = [&](const Chunk& c, u32x4_t* kr, u32x4_t* vr) {
     const int first = c.k >> bs_log2, last = (c.k + c.cnt - 1) >> bs_log2;
     if (c.b != bt_b || first < bt_base || last >= bt_base + 64) {
+      if constexpr (NT) {
+        if (c.b != bt_b) stream_from = kv_stream_from[c.b];
+      }
       bt_b = c.b;
       bt_base = first;
       bt_reg = bt_base + lane < bt_stride ? block_tables[(int64_t)c.b * bt_stride + bt_base + lane] : -1;
@@ -172,30 +179,36 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     // once from the window with a scalar lane read; otherwise each row shuffles its own
     const bool one_block = first == last;
     const int blk0 = __builtin_amdgcn_readlane(bt_reg, min(first - bt_base, 63));
-    const bool nt = NT == 1 || (NT == 2 && first >= kv_stream_from);  // wave-uniform
+    // the chunk's loads as one straight batch per load kind (the choice is wave-uniform)
+    auto loads = [&](auto streamed) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r = i * RPI + rsub;
-      const int j = c.k + r;
-      const int blk = one_block ? blk0 : __shfl(bt_reg, min((j >> bs_log2) - bt_base, 63));
-      kr[i] = u32x4_t{0u, 0u, 0u, 0u};
-      vr[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (r < c.cnt) {
-        if ((unsigned)blk < (unsigned)num_blocks) {
-          const int64_t off = (((int64_t)blk << bs_log2) + (j & bs_mask)) * row_elems + head_off;
-          if (nt) {
-            kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k_cache + off));
-            vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(v_cache + off));
+      for (int i = 0; i < NI; ++i) {
+        const int r = i * RPI + rsub;
+        const int j = c.k + r;
+        const int blk = one_block ? blk0 : __shfl(bt_reg, min((j >> bs_log2) - bt_base, 63));
+        kr[i] = u32x4_t{0u, 0u, 0u, 0u};
+        vr[i] = u32x4_t{0u, 0u, 0u, 0u};
+        if (r < c.cnt) {
+          if ((unsigned)blk < (unsigned)num_blocks) {
+            const int64_t off = (((int64_t)blk << bs_log2) + (j & bs_mask)) * row_elems + head_off;
+            if constexpr (decltype(streamed)::value) {
+              kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k_cache + off));
+              vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(v_cache + off));
+            } else {
+              kr[i] = load16(k_cache + off);
+              vr[i] = load16(v_cache + off);
+            }
           } else {
-            kr[i] = load16(k_cache + off);
-            vr[i] = load16(v_cache + off);
+            kr[i] = E::nan_chunk();
+            vr[i] = E::nan_chunk();
           }
-        } else {
-          kr[i] = E::nan_chunk();
-          vr[i] = E::nan_chunk();
         }
       }
-    }
+    };
+    if (NT && first >= stream_from)
+      loads(std::true_type{});
+    else
+      loads(std::false_type{});
   };
   auto load_q = [&](const Chunk& c, u32x4_t* qw) {
 #pragma unroll
@@ -583,10 +596,8 @@ static int run_decode(const DecodeArgs& a, hipStream_t stream) {
   if (blocks > a.max_workgroups) blocks = a.max_workgroups;
   if (blocks < 1) blocks = 1;
   const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
-  auto* stream_kernel = a.kv_stream_from >= a.max_blocks_per_seq
-                           ? decode_stream_kernel<T, D, G, NI, HPW, 0>
-                           : (a.kv_stream_from == 0 ? decode_stream_kernel<T, D, G, NI, HPW, 1>
-                                                    : decode_stream_kernel<T, D, G, NI, HPW, 2>);
+  auto* stream_kernel = a.kv_stream_from ? decode_stream_kernel<T, D, G, NI, HPW, true>
+                                         : decode_stream_kernel<T, D, G, NI, HPW, false>;
   hipLaunchKernelGGL(stream_kernel, dim3((unsigned)blocks), dim3(256),
                      lds, stream, (T*)a.out, (const T*)a.q, (const T*)a.k_cache,
                      (const T*)a.v_cache, a.num_blocks, a.block_tables, a.max_blocks_per_seq,

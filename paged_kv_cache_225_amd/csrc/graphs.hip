@@ -74,8 +74,8 @@ int pkv_decode_graphs_create(pkv_decode_graphs** handle, int32_t max_batch,
                              const int32_t* context_lens,
                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                              int32_t block_size, float scale, pkv_dtype_t dtype,
-                             int32_t partition_size, int32_t kv_stream_from, void* workspace,
-                             size_t workspace_bytes) {
+                             int32_t partition_size, const int32_t* kv_stream_from,
+                             void* workspace, size_t workspace_bytes) {
   if (!handle) return PKV_ERR_INVALID;
   *handle = nullptr;
   if (max_batch < 1 || max_batch > 16383) return PKV_ERR_INVALID;

@@ -33,7 +33,7 @@ struct DecodeArgs {
   float* ws_ml;             // [num_seqs, Hq, max_parts, 2]
   int32_t* ws_meta;         // [num_seqs + 2]: the share size, then the context prefix sums
   int32_t max_workgroups;   // cap of the decode grid (4 wavefronts each)
-  int32_t kv_stream_from;   // table columns >= this are read with non-temporal loads
+  const int32_t* kv_stream_from;  // [num_seqs] or null: columns >= [b] read non-temporally
   // fused store of the step's tokens (new_k == nullptr: attention only); token b of
   // new_k / new_v is the newest token of sequence b, written to slot slot_mapping[b]
   const void* new_k;

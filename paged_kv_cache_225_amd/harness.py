@@ -39,11 +39,11 @@ def poison_fill_(t: torch.Tensor) -> torch.Tensor:
 
 class DeviceStep:
     def __init__(self, w, device="cuda", fill=None, partition_size=0, table_width=None,
-                 kv_stream_from=B.PKV_KV_STREAM_NONE):
+                 kv_stream_from=None):
         self.w = w
         self.device = torch.device(device)
         self.partition_size = partition_size
-        self.kv_stream_from = kv_stream_from
+        self.kv_stream_spec = kv_stream_from
         tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
         self.k_cache = torch.empty(shape, dtype=tdt, device=self.device)
@@ -104,11 +104,28 @@ class DeviceStep:
         self.new_v = _to_device(nv, w.dtype, dev)
         self.q = _to_device(w.q, w.dtype, dev)
         self.out = torch.empty_like(self.q)
+        self.kv_stream_from = self._stream_from(self.kv_stream_spec)
         if w.kind == "decode":
             nbytes = B.paged_attn_decode_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim,
                                                          self.block_tables.shape[1], w.block_size,
                                                          self.partition_size)
             self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+    def _stream_from(self, spec):
+        """The decode calls' kv_stream_from: None (every K/V row read with ordinary loads), an
+        int (the same first streamed table column for every sequence), "shared" (each
+        sequence's count of leading blocks shared with other sequences, as a block manager's
+        reference counts give it) or a per-sequence array."""
+        if spec is None:
+            return None
+        if isinstance(spec, str):
+            assert spec == "shared", spec
+            arr = np.asarray(self.w.shared_blocks, dtype=np.int32)
+        elif np.isscalar(spec):
+            arr = np.full(self.w.num_seqs, int(spec), dtype=np.int32)
+        else:
+            arr = np.asarray(spec, dtype=np.int32)
+        return _i32(arr, self.device)
 
     def store(self, stream=None):
         B.store_kvcache(self.new_k, self.new_v, self.k_cache, self.v_cache, self.slot_mapping,
@@ -154,7 +171,7 @@ class GraphDecodeStep:
     ``launch(batch)`` replays the bucket's graph."""
 
     def __init__(self, ds: DeviceStep, max_batch: int, width: int = None,
-                 kv_stream_from=B.PKV_KV_STREAM_NONE):
+                 kv_stream_from=None):
         w = ds.w
         assert w.kind == "decode"
         self.ds = ds
@@ -174,9 +191,14 @@ class GraphDecodeStep:
         nbytes = B.paged_attn_decode_workspace_bytes(max_batch, w.num_heads, w.head_dim, width,
                                                      w.block_size, ds.partition_size)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        # per-row first streamed table column, a static buffer the graphs read at replay
+        self.stream_from = None
+        if kv_stream_from is not None:
+            self.stream_from = torch.full((max_batch,), int(kv_stream_from), dtype=torch.int32,
+                                          device=dev)
         self.graphs = B.DecodeGraphs(self.out, self.q, self.key, self.value, self.slots,
                                      ds.k_cache, ds.v_cache, self.tables, self.ctx, w.scale,
-                                     self.workspace, ds.partition_size, kv_stream_from)
+                                     self.workspace, ds.partition_size, self.stream_from)
 
     def load(self, seqs):
         ds, n = self.ds, len(seqs)
@@ -193,11 +215,13 @@ class GraphDecodeStep:
         self.graphs.launch(batch, stream)
         return self.out[:batch]
 
-    def eager(self, batch, out=None, stream=None, kv_stream_from=B.PKV_KV_STREAM_NONE):
+    def eager(self, batch, out=None, stream=None, kv_stream_from="graph"):
         """The recorded call, made eagerly on the same padded buffers (bucket rows)."""
         n = self.graphs.bucket(batch)
         out = self.out if out is None else out
         ds = self.ds
+        if isinstance(kv_stream_from, str):  # "graph": the recorded calls' buffer
+            kv_stream_from = None if self.stream_from is None else self.stream_from[:n]
         B.paged_attn_decode_store(out[:n], self.q[:n], self.key[:n], self.value[:n],
                                   self.slots[:n], ds.k_cache, ds.v_cache, self.tables[:n],
                                   self.ctx[:n], ds.w.scale, workspace=self.workspace,

@@ -118,7 +118,7 @@ FAKE = ctypes.c_void_p(0x1000)
 
 def _decode_rc(**kw):
     a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=16, bt=FAKE, W=4, ctx=FAKE, B=2, Hq=4, Hkv=2,
-             D=128, bs=256, scale=0.1, dt=B.PKV_BF16, part=0, ksf=B.PKV_KV_STREAM_NONE, ws=FAKE,
+             D=128, bs=256, scale=0.1, dt=B.PKV_BF16, part=0, ksf=None, ws=FAKE,
              ws_bytes=1 << 30)
     a.update(kw)
     return B.load_library().paged_attn_decode(a["out"], a["q"], a["k"], a["v"], a["nb"], a["bt"],
@@ -130,7 +130,7 @@ def _decode_rc(**kw):
 def _decode_store_rc(**kw):
     a = dict(out=FAKE, q=FAKE, key=FAKE, ks=1024, value=FAKE, vs=1024, slots=FAKE, k=FAKE, v=FAKE,
              nb=16, bt=FAKE, W=4, ctx=FAKE, B=2, Hq=16, Hkv=8, D=128, bs=256, scale=0.1,
-             dt=B.PKV_BF16, part=0, ksf=B.PKV_KV_STREAM_NONE, ws=FAKE, ws_bytes=1 << 30)
+             dt=B.PKV_BF16, part=0, ksf=None, ws=FAKE, ws_bytes=1 << 30)
     a.update(kw)
     return B.load_library().paged_attn_decode_store(
         a["out"], a["q"], a["key"], a["ks"], a["value"], a["vs"], a["slots"], a["k"], a["v"],
@@ -144,7 +144,7 @@ def _decode_store_rc(**kw):
     (dict(ks=1028), -1),                                  # 2056-byte stride: not 16-byte rows
     (dict(key=ctypes.c_void_p(0x1004)), -1), (dict(value=ctypes.c_void_p(0x1008)), -1),
     (dict(dt=7), -2), (dict(D=96), -2), (dict(ws_bytes=16), -3), (dict(B=0), 0),
-    (dict(B=0, key=None), 0), (dict(ksf=-1), -1),
+    (dict(B=0, key=None), 0),
 ])
 def test_decode_store_argument_validation(kw, status):
     assert _decode_store_rc(**kw) == status
@@ -164,7 +164,7 @@ def _prefill_rc(**kw):
     (dict(D=96), -2), (dict(Hq=6, Hkv=2), -2), (dict(Hq=5, Hkv=2), -1), (dict(bs=24), -2),
     (dict(bs=8), -2), (dict(dt=7), -2), (dict(part=100), -1), (dict(part=2048), -1),
     (dict(ws_bytes=16), -3), (dict(ws=None), -3), (dict(q=None), -1), (dict(B=0), 0),
-    (dict(W=0), -1), (dict(nb=0), -1), (dict(ksf=-1), -1), (dict(ksf=-5, B=0), -1),
+    (dict(W=0), -1), (dict(nb=0), -1),
     # 16-byte vector rows: misaligned out, q, caches or workspace are rejected
     (dict(out=ctypes.c_void_p(0x1002)), -1), (dict(q=ctypes.c_void_p(0x1008)), -1),
     (dict(k=ctypes.c_void_p(0x1004)), -1), (dict(v=ctypes.c_void_p(0x100c)), -1),
@@ -235,7 +235,7 @@ def test_decode_graphs_argument_validation():
     lib = B.load_library()
     h = ctypes.c_void_p()
     args = [FAKE, FAKE, FAKE, 1024, FAKE, 1024, FAKE, FAKE, FAKE, 16, FAKE, 16, FAKE,
-            16, 8, 128, 256, 0.1, B.PKV_BF16, 0, B.PKV_KV_STREAM_NONE]
+            16, 8, 128, 256, 0.1, B.PKV_BF16, 0, None]
     assert lib.pkv_decode_graphs_create(None, 4, *args, FAKE, 1 << 30) == -1
     assert lib.pkv_decode_graphs_create(ctypes.byref(h), 0, *args, FAKE, 1 << 30) == -1
     assert lib.pkv_decode_graphs_create(ctypes.byref(h), 16384, *args, FAKE, 1 << 30) == -1

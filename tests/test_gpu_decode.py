@@ -137,12 +137,14 @@ def test_decode_few_row_combine_is_bitwise_the_general_one(Hq, Hkv, D):
 @pytest.mark.parametrize("cfg,fused", [(2, False), (2, True), (1, False), (5, False), (5, True)])
 def test_decode_kv_stream_from_is_bitwise_neutral(cfg, fused):
     """kv_stream_from changes only how the K/V rows pass the caches: outputs and the cache
-    written by the fused store are bit for bit the same whether no column, every column or
-    the columns past the shared prefix are streamed."""
+    written by the fused store are bit for bit the same whether no row, every row, the rows
+    past each sequence's shared prefix, or a random per-sequence choice is streamed."""
     w = make_config(cfg)
+    rng = np.random.default_rng(cfg)
+    specs = [None, 0, "shared", rng.integers(-2, w.max_table_len() + 2, w.num_seqs), 1 << 30]
     outs, pools = [], []
-    for ksf in (B.PKV_KV_STREAM_NONE, B.PKV_KV_STREAM_ALL, 8, 1):
-        ds = DeviceStep(w, kv_stream_from=ksf)
+    for spec in specs:
+        ds = DeviceStep(w, kv_stream_from=spec)
         (ds.step_fused if fused else ds.step)()
         torch.cuda.synchronize()
         outs.append(ds.out.clone())

@@ -121,12 +121,12 @@ def test_graph_decode_lengths_change_between_replays():
 
 
 def test_graph_recorded_with_streaming_loads():
-    """Graphs recorded with every K/V row streamed (kv_stream_from 0) replay correctly: the
-    replay matches the oracle and equals, bit for bit, the eager call made with either load
-    choice (the loads never change the arithmetic)."""
+    """Graphs recorded with a per-row kv_stream_from buffer (every K/V row streamed) replay
+    correctly: the replay matches the oracle and equals, bit for bit, the eager call made
+    with the buffer or with no streaming at all (the loads never change the arithmetic)."""
     w = make_config(2)
     ds = DeviceStep(w, table_width=W)
-    st = GraphDecodeStep(ds, 64, kv_stream_from=B.PKV_KV_STREAM_ALL)
+    st = GraphDecodeStep(ds, 64, kv_stream_from=0)
     ref, _, _, _ = run_workload(w)
     stream = torch.cuda.current_stream()
     seqs = np.random.Generator(np.random.PCG64(9)).choice(w.num_seqs, size=40, replace=False)
@@ -137,7 +137,7 @@ def test_graph_recorded_with_streaming_loads():
     torch.cuda.synchronize()
     assert_attention_close(st.out[:40].double().cpu().numpy(), ref[seqs], label="streaming graph")
     first = st.out[:bucket].clone()
-    for ksf in (B.PKV_KV_STREAM_NONE, B.PKV_KV_STREAM_ALL):
+    for ksf in (None, "graph"):
         eager = torch.empty_like(st.out)
         st.eager(40, out=eager, stream=stream, kv_stream_from=ksf)
         torch.cuda.synchronize()

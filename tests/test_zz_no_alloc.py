@@ -46,7 +46,8 @@ def test_noalloc_decode_fp32_and_streamed_rows():
     ds = DeviceStep(w)
     ds.store()
     ref, _, _, _ = run_workload(w)
-    for ksf in (B.PKV_KV_STREAM_NONE, B.PKV_KV_STREAM_ALL):
+    zeros = torch.zeros(w.num_seqs, dtype=torch.int32, device=ds.q.device)
+    for ksf in (None, zeros):
         got = torch.full_like(ds.out, float("nan"))
         B.paged_attn_decode_noalloc(got, ds.q, ds.k_cache, ds.v_cache, ds.block_tables,
                                     ds.context_lens, w.scale, kv_stream_from=ksf)
