@@ -12,7 +12,8 @@ streams from HBM rather than from the 256 MB last-level cache.
 The same JSON line also carries the prefill half of the metric (the varlen prefill, the
 prefix-cached prefill and the chunked prefill workloads, in TFLOP/s against the bf16 MFMA
 peak), the large decode workload (512 sequences, shared prefixes), small-batch decode steps
-replayed from recorded graphs next to eager calls, and the host metadata time.
+replayed from recorded graphs next to eager calls (one call, and a whole 28-layer step), and
+the host metadata time.
 
 ``value`` is the decode step's algorithmic bytes per second (KV rows of every visible key
 once per sequence and kv head, plus q, out, tables, and the store's reads and writes).
@@ -307,6 +308,69 @@ def bench_graph_decode(torch, iters):
             "steps": rows}
 
 
+def bench_graph_decode_layers(torch, iters, num_layers=28):
+    """A whole decode step of a 28-layer model (Qwen3-0.6B's depth): one
+    paged_attn_decode_store per layer, each layer its own 2048-block pool (device copies of
+    the batch-64 workload's pool) and rows over the step's shared metadata. The graph leg
+    replays one recorded graph per step (every layer's call); the eager leg makes the 28
+    library calls from Python, as an engine without graphs does. Wall time per step over
+    `iters` back-to-back steps, batches of 1, 4, 16 and 64 sequences."""
+    from paged_kv_cache_225_amd import _binding as B
+    from paged_kv_cache_225_amd.harness import DeviceStep, LayeredGraphDecodeStep
+    from workloads import make_config
+    w = make_config(2)
+    ds = DeviceStep(w)
+    layers = [ds] + [ds.replica() for _ in range(num_layers - 1)]
+    gs = LayeredGraphDecodeStep(layers, 64, width=16)
+    stream = torch.cuda.current_stream()
+    rng = np.random.Generator(np.random.PCG64(78))
+    gs.load(np.arange(64))
+    for n in gs.graphs.buckets:
+        for _ in range(10):
+            gs.launch(n, stream)
+    torch.cuda.synchronize()
+    rows = []
+    for b in (1, 4, 16, 64):
+        seqs = rng.choice(w.num_seqs, size=b, replace=False)
+        gs.load(seqs)
+        n = gs.graphs.bucket(b)
+
+        def eager():
+            for l, d in enumerate(layers):
+                B.paged_attn_decode_store(gs.out[l][:b], gs.q[l][:b], gs.key[l][:b],
+                                          gs.value[l][:b], gs.slots[:b], d.k_cache, d.v_cache,
+                                          gs.tables[:b], gs.ctx[:b], w.scale,
+                                          workspace=gs.workspace, stream=stream)
+
+        def graph():
+            gs.launch(b, stream)
+
+        res = {"batch": b, "bucket": n}
+        for name, fn in (("eager", eager), ("graph", graph)):
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(iters):
+                fn()
+            t_host = time.perf_counter() - t0
+            torch.cuda.synchronize()
+            res[name + "_us_per_step"] = (time.perf_counter() - t0) / iters * 1e6
+            res[name + "_host_us_per_step"] = t_host / iters * 1e6
+        res["graph_speedup"] = res["eager_us_per_step"] / res["graph_us_per_step"]
+        rows.append(res)
+    gs.graphs.close()
+    del gs, layers, ds
+    torch.cuda.empty_cache()
+    return {"workload": f"{num_layers}-layer decode step: per layer one paged_attn_decode_store "
+                        "over its own 2048-block pool; 1/4/16/64 sequences of the batch-64 "
+                        "workload (ctx U[256,4096], 16q/8kv heads, d128, bf16)",
+            "note": "wall time per step over back-to-back steps; eager: 28 library calls "
+                    "from Python per step; graph: one graph launch per step; host_us: the "
+                    "enqueue loop's time per step before the final wait",
+            "layers": num_layers, "steps": rows}
+
+
 def bench_sampler(torch, iters):
     """Temperature sampling of one decode step's next tokens: 64 rows of Qwen3-vocabulary
     (151936) fp32 logits, the row's logits read once (HBM bytes = rows x vocab x 4)."""
@@ -430,7 +494,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true",
                     help="secondary workloads: skip the 1 GiB cache flush between timed runs")
     ap.add_argument("--only", choices=["prefill3", "prefill4", "prefill3packed", "chunked", "large",
-                                       "tiny", "graph", "sampler"], default=None,
+                                       "tiny", "graph", "graph_layers", "sampler"],
+                    default=None,
                     help="run one secondary workload alone (for profiler passes)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -458,6 +523,8 @@ def main():
             res = bench_prefill(torch, "chunked", args.iters, 5, flush)
         elif args.only == "graph":
             res = bench_graph_decode(torch, 200)
+        elif args.only == "graph_layers":
+            res = bench_graph_decode_layers(torch, args.iters)
         elif args.only == "sampler":
             res = bench_sampler(torch, args.iters)
         else:
@@ -511,6 +578,8 @@ def main():
         line["tiny_decode"] = bench_tiny_decode(torch, args.iters, 5, flush)
         print("bench: graph-replayed small-batch decode", file=sys.stderr, flush=True)
         line["graph_decode"] = bench_graph_decode(torch, 200)
+        print("bench: graph-replayed 28-layer decode steps", file=sys.stderr, flush=True)
+        line["graph_decode_layers"] = bench_graph_decode_layers(torch, args.iters)
         print("bench: sampler", file=sys.stderr, flush=True)
         line["sampler"] = bench_sampler(torch, args.iters)
     if not args.no_cpu_baseline:

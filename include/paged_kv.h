@@ -266,6 +266,18 @@ int paged_attn_decode_store(void* out, const void* q,
  * 1 .. max_batch), PKV_ERR_WORKSPACE, any status paged_attn_decode_store returns for the
  * recorded call, PKV_ERR_HIP (capture, instantiation or launch failed). On error, create
  * leaves *handle NULL and frees what it made.
+ *
+ * pkv_decode_graphs_create_layers records a whole decode step of a model with num_layers
+ * attention layers, the unit [P1] capture_cudagraph records: each bucket's graph holds
+ * num_layers paged_attn_decode_store calls in layer order on one stream. Every layer has
+ * its own pool and its own rows: out[l], q[l], key[l], value[l], k_cache[l], v_cache[l] are
+ * host arrays of num_layers device pointers (read during the call only; the buffers they
+ * name are as above, one set per layer). slot_mapping, block_tables, context_lens and
+ * kv_stream_from are shared by all layers, as every layer of [P1]'s model reads the one
+ * step Context (one block id names the same block in every layer's pool). The layers run
+ * one after another and share the workspace. pkv_decode_graphs_create is this call with
+ * num_layers 1. Errors as above, plus PKV_ERR_INVALID for num_layers outside 1 .. 1024 or
+ * a null pointer array.
  * -------------------------------------------------------------------------------------*/
 typedef struct pkv_decode_graphs pkv_decode_graphs;
 
@@ -281,6 +293,20 @@ int pkv_decode_graphs_create(pkv_decode_graphs** handle, int32_t max_batch,
                              int32_t block_size, float scale, pkv_dtype_t dtype,
                              int32_t partition_size, const int32_t* kv_stream_from,
                              void* workspace, size_t workspace_bytes);
+int pkv_decode_graphs_create_layers(pkv_decode_graphs** handle, int32_t max_batch,
+                                    int32_t num_layers,
+                                    void* const* out, const void* const* q,
+                                    const void* const* key, int64_t key_token_stride,
+                                    const void* const* value, int64_t value_token_stride,
+                                    const int32_t* slot_mapping,
+                                    void* const* k_cache, void* const* v_cache,
+                                    int32_t num_blocks,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens,
+                                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, float scale, pkv_dtype_t dtype,
+                                    int32_t partition_size, const int32_t* kv_stream_from,
+                                    void* workspace, size_t workspace_bytes);
 int pkv_decode_graphs_count(const pkv_decode_graphs* handle);
 int pkv_decode_graphs_buckets(const pkv_decode_graphs* handle, int32_t* buckets,
                               int32_t capacity);

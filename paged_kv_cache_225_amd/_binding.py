@@ -43,6 +43,11 @@ SIGNATURES = {
     "pkv_decode_graphs_create": (_c_int, [ctypes.POINTER(_p), _i32, _p, _p, _p, _i64, _p, _i64,
                                           _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32,
                                           _i32, _f, _c_int, _i32, _p, _p, _size]),
+    "pkv_decode_graphs_create_layers": (_c_int, [ctypes.POINTER(_p), _i32, _i32, ctypes.POINTER(_p), ctypes.POINTER(_p),
+                                                 ctypes.POINTER(_p), _i64, ctypes.POINTER(_p), _i64, _p, ctypes.POINTER(_p),
+                                                 ctypes.POINTER(_p), _i32, _p, _i32, _p, _i32, _i32,
+                                                 _i32, _i32, _f, _c_int, _i32, _p, _p,
+                                                 _size]),
     "pkv_decode_graphs_count": (_c_int, [_p]),
     "pkv_decode_graphs_buckets": (_c_int, [_p, _p, _i32]),
     "pkv_decode_graphs_bucket": (_c_int, [_p, _i32]),
@@ -308,31 +313,63 @@ def attn_prefill_varlen(out, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, 
 
 
 class DecodeGraphs:
-    """pkv_decode_graphs_*: one recorded paged_attn_decode_store call per batch bucket over
-    static device buffers sized for max_batch rows (the tensors are kept alive here, since
-    the graphs hold their addresses). ``launch(B)`` replays the smallest bucket >= B on the
-    stream; the caller has written rows 0 .. B-1 and padded rows B .. bucket-1 with
-    context_lens 0 and slot_mapping -1 (``pad`` does that)."""
+    """pkv_decode_graphs_*: recorded decode steps, one graph per batch bucket, over static
+    device buffers sized for max_batch rows (the tensors are kept alive here, since the
+    graphs hold their addresses). Given tensors, each graph holds one
+    paged_attn_decode_store call (pkv_decode_graphs_create); given equal-length lists of
+    per-layer tensors for out, q, key, value, k_cache and v_cache, it holds one call per
+    layer in order (pkv_decode_graphs_create_layers), the metadata buffers being shared.
+    ``launch(B)`` replays the smallest bucket >= B on the stream; the caller has written
+    rows 0 .. B-1 and padded rows B .. bucket-1 with context_lens 0 and slot_mapping -1
+    (``pad`` does that)."""
 
     def __init__(self, out, q, key, value, slot_mapping, k_cache, v_cache, block_tables,
                  context_lens, scale, workspace, partition_size=0,
                  kv_stream_from=None):
-        max_batch, Hq, D = q.shape
-        num_blocks, bs, Hkv, _ = k_cache.shape
-        if key.stride(2) != 1 or key.stride(1) != D or value.stride(2) != 1 or value.stride(1) != D:
-            raise ValueError("key/value need head stride head_dim and unit element stride")
-        self._keep = (out, q, key, value, slot_mapping, k_cache, v_cache, block_tables,
-                      context_lens, workspace)
+        layered = isinstance(q, (list, tuple))
+        per_layer = [out, q, key, value, k_cache, v_cache]
+        if layered:
+            n = len(q)
+            if n == 0 or any(not isinstance(t, (list, tuple)) or len(t) != n for t in per_layer):
+                raise ValueError("out, q, key, value, k_cache, v_cache: lists of one length")
+        else:
+            per_layer = [[t] for t in per_layer]
+        outs, qs, keys, values, kcs, vcs = per_layer
+        max_batch, Hq, D = qs[0].shape
+        num_blocks, bs, Hkv, _ = kcs[0].shape
+        for l in range(len(qs)):
+            if qs[l].shape != qs[0].shape or kcs[l].shape != kcs[0].shape or \
+                    vcs[l].shape != kcs[0].shape or outs[l].shape != qs[0].shape:
+                raise ValueError(f"layer {l}: shapes differ from layer 0")
+            for t in (keys[l], values[l]):
+                if t.stride(2) != 1 or t.stride(1) != D or t.stride(0) != keys[0].stride(0):
+                    raise ValueError("key/value need head stride head_dim, unit element "
+                                     "stride and one token stride across layers")
+        self._keep = (outs, qs, keys, values, slot_mapping, kcs, vcs, block_tables,
+                      context_lens, workspace, kv_stream_from)
         self.slot_mapping, self.context_lens = slot_mapping, context_lens
+        self.num_layers = len(qs)
         ws_bytes = workspace.numel() * workspace.element_size()
+        lib = load_library()
         h = _p()
-        rc = load_library().pkv_decode_graphs_create(
-            ctypes.byref(h), max_batch, _t_ptr(out), _t_ptr(q), _t_ptr(key), key.stride(0),
-            _t_ptr(value), value.stride(0), _t_ptr(slot_mapping), _t_ptr(k_cache),
-            _t_ptr(v_cache), num_blocks, _t_ptr(block_tables), block_tables.shape[1],
-            _t_ptr(context_lens), Hq, Hkv, D, bs, float(scale), _dtype_code(q), partition_size,
-            _t_ptr(kv_stream_from), _t_ptr(workspace), ws_bytes)
-        _check("pkv_decode_graphs_create", rc)
+        common = (_t_ptr(slot_mapping),)
+        tail = (num_blocks, _t_ptr(block_tables), block_tables.shape[1], _t_ptr(context_lens),
+                Hq, Hkv, D, bs, float(scale), _dtype_code(qs[0]), partition_size,
+                _t_ptr(kv_stream_from), _t_ptr(workspace), ws_bytes)
+        if not layered:
+            rc = lib.pkv_decode_graphs_create(
+                ctypes.byref(h), max_batch, _t_ptr(out), _t_ptr(q), _t_ptr(key), key.stride(0),
+                _t_ptr(value), value.stride(0), *common, _t_ptr(k_cache), _t_ptr(v_cache),
+                *tail)
+            _check("pkv_decode_graphs_create", rc)
+        else:
+            def arr(ts):
+                return (_p * len(ts))(*[t.data_ptr() for t in ts])
+            rc = lib.pkv_decode_graphs_create_layers(
+                ctypes.byref(h), max_batch, self.num_layers, arr(outs), arr(qs), arr(keys),
+                keys[0].stride(0), arr(values), values[0].stride(0), *common, arr(kcs),
+                arr(vcs), *tail)
+            _check("pkv_decode_graphs_create_layers", rc)
         self._h = h
         self.max_batch = max_batch
 

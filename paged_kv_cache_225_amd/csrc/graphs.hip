@@ -8,8 +8,11 @@
 // 手撕笔记" (cuda graph捕捉与context设置) gives the reason: the shapes and device addresses a
 // graph records are fixed, and one launch of the graph replaces the step's kernel launches.
 //
-// Here each graph holds one paged_attn_decode_store call (the decode kernels with the store
-// fused in) at that bucket's row count. The launch configuration depends only on the row
+// Here each graph holds, for every attention layer of the model, one paged_attn_decode_store
+// call (the decode kernels with the store fused in) at that bucket's row count: the engine's
+// graph covers the whole forward, so one launch replaces the launches of every layer.
+// Layers have their own pools and rows but share the step's metadata (slot_mapping, block
+// tables, context lengths), as all layers of that model read one Context. The launch configuration depends only on the row
 // count and the static table width, and everything that depends on the data (shares of the
 // split, piece counts) is computed on the device from context_lens at run time, so a
 // recorded call stays correct for any lengths written into the buffers before a replay.
@@ -26,6 +29,7 @@
 
 struct pkv_decode_graphs {
   int32_t max_batch = 0;
+  int32_t num_layers = 0;
   std::vector<int32_t> buckets;     // ascending
   std::vector<hipGraph_t> graphs;   // one per bucket
   std::vector<hipGraphExec_t> execs;
@@ -64,21 +68,25 @@ int bucket_index(const pkv_decode_graphs* g, int32_t batch) {
 
 extern "C" {
 
-int pkv_decode_graphs_create(pkv_decode_graphs** handle, int32_t max_batch,
-                             void* out, const void* q,
-                             const void* key, int64_t key_token_stride,
-                             const void* value, int64_t value_token_stride,
-                             const int32_t* slot_mapping,
-                             void* k_cache, void* v_cache, int32_t num_blocks,
-                             const int32_t* block_tables, int32_t max_blocks_per_seq,
-                             const int32_t* context_lens,
-                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                             int32_t block_size, float scale, pkv_dtype_t dtype,
-                             int32_t partition_size, const int32_t* kv_stream_from,
-                             void* workspace, size_t workspace_bytes) {
+int pkv_decode_graphs_create_layers(pkv_decode_graphs** handle, int32_t max_batch,
+                                    int32_t num_layers,
+                                    void* const* out, const void* const* q,
+                                    const void* const* key, int64_t key_token_stride,
+                                    const void* const* value, int64_t value_token_stride,
+                                    const int32_t* slot_mapping,
+                                    void* const* k_cache, void* const* v_cache,
+                                    int32_t num_blocks,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens,
+                                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, float scale, pkv_dtype_t dtype,
+                                    int32_t partition_size, const int32_t* kv_stream_from,
+                                    void* workspace, size_t workspace_bytes) {
   if (!handle) return PKV_ERR_INVALID;
   *handle = nullptr;
   if (max_batch < 1 || max_batch > 16383) return PKV_ERR_INVALID;
+  if (num_layers < 1 || num_layers > 1024) return PKV_ERR_INVALID;
+  if (!out || !q || !key || !value || !k_cache || !v_cache) return PKV_ERR_INVALID;
   const size_t need = paged_attn_decode_workspace_bytes(max_batch, num_heads, head_dim,
                                                         max_blocks_per_seq, block_size,
                                                         partition_size);
@@ -88,6 +96,7 @@ int pkv_decode_graphs_create(pkv_decode_graphs** handle, int32_t max_batch,
   pkv_decode_graphs* g = new (std::nothrow) pkv_decode_graphs;
   if (!g) return PKV_ERR_HIP;
   g->max_batch = max_batch;
+  g->num_layers = num_layers;
   g->buckets = bucket_list(max_batch);
 
   hipStream_t cs = nullptr;  // a private stream to record on (default priority)
@@ -104,11 +113,13 @@ int pkv_decode_graphs_create(pkv_decode_graphs** handle, int32_t max_batch,
       rc = PKV_ERR_HIP;
       break;
     }
-    const int call = paged_attn_decode_store(
-        out, q, key, key_token_stride, value, value_token_stride, slot_mapping, k_cache,
-        v_cache, num_blocks, block_tables, max_blocks_per_seq, context_lens, bs, num_heads,
-        num_kv_heads, head_dim, block_size, scale, dtype, partition_size, kv_stream_from,
-        workspace, workspace_bytes, cs);
+    int call = PKV_OK;
+    for (int32_t l = 0; l < num_layers && call == PKV_OK; ++l)
+      call = paged_attn_decode_store(
+          out[l], q[l], key[l], key_token_stride, value[l], value_token_stride, slot_mapping,
+          k_cache[l], v_cache[l], num_blocks, block_tables, max_blocks_per_seq, context_lens,
+          bs, num_heads, num_kv_heads, head_dim, block_size, scale, dtype, partition_size,
+          kv_stream_from, workspace, workspace_bytes, cs);
     const hipError_t end = hipStreamEndCapture(cs, &graph);
     if (call != PKV_OK || end != hipSuccess || !graph) {
       if (graph) (void)hipGraphDestroy(graph);
@@ -131,6 +142,25 @@ int pkv_decode_graphs_create(pkv_decode_graphs** handle, int32_t max_batch,
   }
   *handle = g;
   return PKV_OK;
+}
+
+int pkv_decode_graphs_create(pkv_decode_graphs** handle, int32_t max_batch,
+                             void* out, const void* q,
+                             const void* key, int64_t key_token_stride,
+                             const void* value, int64_t value_token_stride,
+                             const int32_t* slot_mapping,
+                             void* k_cache, void* v_cache, int32_t num_blocks,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens,
+                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, float scale, pkv_dtype_t dtype,
+                             int32_t partition_size, const int32_t* kv_stream_from,
+                             void* workspace, size_t workspace_bytes) {
+  return pkv_decode_graphs_create_layers(
+      handle, max_batch, 1, &out, &q, &key, key_token_stride, &value, value_token_stride,
+      slot_mapping, &k_cache, &v_cache, num_blocks, block_tables, max_blocks_per_seq,
+      context_lens, num_heads, num_kv_heads, head_dim, block_size, scale, dtype,
+      partition_size, kv_stream_from, workspace, workspace_bytes);
 }
 
 int pkv_decode_graphs_count(const pkv_decode_graphs* g) {

@@ -9,9 +9,13 @@ arbitrary bits), makes the resident tokens resident with the library's own metad
 ``paged_attn_decode_store`` call. Host metadata is built by the library's host calls.
 ``GraphDecodeStep`` replays decode steps of any subset of a ``DeviceStep``'s sequences from
 the library's recorded graphs, the way the engine's run_model does (static buffers, padded
-rows, the smallest bucket that fits).
+rows, the smallest bucket that fits). ``LayeredGraphDecodeStep`` does the same for a model
+of several attention layers (one ``DeviceStep`` per layer over the same metadata), one
+recorded graph covering every layer's call.
 """
 from __future__ import annotations
+
+import copy
 
 import numpy as np
 import torch
@@ -159,6 +163,14 @@ class DeviceStep:
                                   kv_stream_from=self.kv_stream_from, stream=stream)
         return self.out
 
+    def replica(self) -> "DeviceStep":
+        """Another layer over the same step: its own pool and rows, device copies of these
+        (same metadata tensors, shared)."""
+        r = copy.copy(self)
+        for name in ("k_cache", "v_cache", "q", "new_k", "new_v", "out"):
+            setattr(r, name, getattr(self, name).clone())
+        return r
+
     def out_f64(self) -> np.ndarray:
         o = self.out.float().cpu().numpy() if self.out.dtype == torch.bfloat16 else self.out.cpu().numpy()
         return o.astype(np.float64)
@@ -228,3 +240,76 @@ class GraphDecodeStep:
                                   partition_size=ds.partition_size,
                                   kv_stream_from=kv_stream_from, stream=stream)
         return out[:batch]
+
+
+class LayeredGraphDecodeStep:
+    """Static buffers of max_batch rows for each of several layers, with the library's decode
+    graphs recorded over all of them (``pkv_decode_graphs_create_layers``): one replay runs
+    every layer's paged_attn_decode_store in order. ``layers`` are DeviceSteps of one step
+    (same sequences, lengths and block tables; each its own pool and rows); the metadata
+    buffers are shared by the layers, as the engine's one Context is."""
+
+    def __init__(self, layers, max_batch: int, width: int = None, kv_stream_from=None):
+        ds0 = layers[0]
+        w = ds0.w
+        assert w.kind == "decode"
+        for ds in layers[1:]:
+            assert torch.equal(ds.block_tables, ds0.block_tables)
+            assert torch.equal(ds.context_lens, ds0.context_lens)
+            assert torch.equal(ds.slot_mapping, ds0.slot_mapping)
+        self.layers = layers
+        width = ds0.block_tables.shape[1] if width is None else width
+        assert width >= ds0.block_tables.shape[1]
+        dev = ds0.q.device
+        Hq, D = ds0.q.shape[1:]
+        Hkv = ds0.new_k.shape[1]
+        dt = ds0.q.dtype
+        self.out = [torch.zeros(max_batch, Hq, D, dtype=dt, device=dev) for _ in layers]
+        self.q = [torch.zeros(max_batch, Hq, D, dtype=dt, device=dev) for _ in layers]
+        self.key = [torch.zeros(max_batch, Hkv, D, dtype=dt, device=dev) for _ in layers]
+        self.value = [torch.zeros(max_batch, Hkv, D, dtype=dt, device=dev) for _ in layers]
+        self.slots = torch.full((max_batch,), -1, dtype=torch.int32, device=dev)
+        self.ctx = torch.zeros(max_batch, dtype=torch.int32, device=dev)
+        self.tables = torch.full((max_batch, width), 1 << 30, dtype=torch.int32, device=dev)
+        nbytes = B.paged_attn_decode_workspace_bytes(max_batch, w.num_heads, w.head_dim, width,
+                                                     w.block_size, ds0.partition_size)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.stream_from = None
+        if kv_stream_from is not None:
+            self.stream_from = torch.full((max_batch,), int(kv_stream_from), dtype=torch.int32,
+                                          device=dev)
+        self.graphs = B.DecodeGraphs(self.out, self.q, self.key, self.value, self.slots,
+                                     [ds.k_cache for ds in layers],
+                                     [ds.v_cache for ds in layers], self.tables, self.ctx,
+                                     w.scale, self.workspace, ds0.partition_size,
+                                     self.stream_from)
+
+    def load(self, seqs):
+        ds0, n = self.layers[0], len(seqs)
+        idx = torch.as_tensor(np.asarray(seqs), dtype=torch.long, device=ds0.q.device)
+        for l, ds in enumerate(self.layers):
+            self.q[l][:n] = ds.q[idx]
+            self.key[l][:n] = ds.new_k[idx]
+            self.value[l][:n] = ds.new_v[idx]
+        self.slots[:n] = ds0.slot_mapping[idx]
+        self.ctx[:n] = ds0.context_lens[idx]
+        self.tables[:n, :ds0.block_tables.shape[1]] = ds0.block_tables[idx]
+        self.graphs.pad(n)
+
+    def launch(self, batch, stream=None):
+        self.graphs.launch(batch, stream)
+        return [o[:batch] for o in self.out]
+
+    def eager(self, batch, out=None, stream=None):
+        """The recorded calls, made eagerly, layer by layer, on the same padded buffers."""
+        n = self.graphs.bucket(batch)
+        out = self.out if out is None else out
+        ksf = None if self.stream_from is None else self.stream_from[:n]
+        for l, ds in enumerate(self.layers):
+            B.paged_attn_decode_store(out[l][:n], self.q[l][:n], self.key[l][:n],
+                                      self.value[l][:n], self.slots[:n], ds.k_cache,
+                                      ds.v_cache, self.tables[:n], self.ctx[:n], ds.w.scale,
+                                      workspace=self.workspace,
+                                      partition_size=ds.partition_size, kv_stream_from=ksf,
+                                      stream=stream)
+        return [o[:batch] for o in out]

@@ -249,6 +249,30 @@ def test_decode_graphs_argument_validation():
     assert lib.pkv_decode_graphs_destroy(None) == -1
 
 
+def test_layered_decode_graphs_argument_validation():
+    # the layered recording: the same checks, plus the layer count and the pointer arrays
+    lib = B.load_library()
+    h = ctypes.c_void_p()
+    arr = (ctypes.c_void_p * 3)(0x1000, 0x2000, 0x3000)
+    tail = [16, FAKE, 16, FAKE, 16, 8, 128, 256, 0.1, B.PKV_BF16, 0, None]
+
+    def call(handle=ctypes.byref(h), max_batch=4, layers=3, out=arr, q=arr, key=arr,
+             value=arr, kc=arr, vc=arr, ws=FAKE, ws_bytes=1 << 30):
+        return lib.pkv_decode_graphs_create_layers(handle, max_batch, layers, out, q, key, 1024,
+                                                   value, 1024, FAKE, kc, vc, *tail, ws,
+                                                   ws_bytes)
+
+    assert call(handle=None) == -1
+    assert call(layers=0) == -1
+    assert call(layers=1025) == -1
+    assert call(max_batch=0) == -1
+    for k in ("out", "q", "key", "value", "kc", "vc"):
+        assert call(**{k: None}) == -1, k
+    assert call(ws_bytes=16) == -3
+    assert call(ws=None) == -3
+    assert h.value is None
+
+
 @pytest.mark.parametrize("W,bs", [(16, 256), (12, 256), (3, 256), (40, 16), (1, 64)])
 def test_default_workspace_covers_every_smaller_batch(W, bs):
     # one workspace sized for n sequences must serve any call with fewer (the decode graphs

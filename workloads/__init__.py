@@ -8,6 +8,7 @@ from .synth import (  # noqa: F401
     Workload,
     CONFIG_NAMES,
     make_config,
+    another_layer,
     make_decode,
     make_prefill,
     make_chunked_prefill,

@@ -24,7 +24,7 @@ gather and no attention, so it carries none of the method's arithmetic.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 
@@ -218,6 +218,20 @@ def make_prefill(seed, q_lens, cached=None, *, Hq, Hkv, D, dtype="bf16", bs=256,
                   Hkv=Hkv, D=D, bs=bs, num_blocks=num_blocks,
                   scale=(1.0 / np.sqrt(D)) if scale is None else scale,
                   shared_blocks=shared_blocks, n_prefix_blocks=n_prefix_blocks, q_mult=q_mult)
+
+
+def another_layer(w: Workload, seed: int, q_mult: float = 1.0) -> Workload:
+    """The same sequences, lengths and block tables with fresh values: a second attention
+    layer of the model, whose pool is indexed by the same block ids (each layer has its own
+    K/V and query rows). Values from PCG64(seed), drawn as the workload's own."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return replace(
+        w, name=f"{w.name}_layer{seed}",
+        prefix_k=_values(rng, w.prefix_k.shape, w.dtype),
+        prefix_v=_values(rng, w.prefix_v.shape, w.dtype),
+        priv_k=_values(rng, w.priv_k.shape, w.dtype),
+        priv_v=_values(rng, w.priv_v.shape, w.dtype),
+        q=_values(rng, w.q.shape, w.dtype, q_mult), meta=dict(w.meta))
 
 
 def make_config(i: int, q_mult: float = 1.0) -> Workload:
