@@ -23,7 +23,8 @@
  *     Host-checkable argument errors are reported before anything is enqueued.
  *     Data-dependent preconditions (slot and block-id ranges, lengths) are documented
  *     per call; the kernels bounds-check them so that a violation never reads or writes
- *     outside the caller's arrays (see each call for what it does instead).
+ *     outside the caller's arrays (see each call for what it does instead). pkv_check_*
+ *     (near the end of this file) test them on request and name the first violation.
  */
 #ifndef PAGED_KV_H_
 #define PAGED_KV_H_
@@ -36,14 +37,24 @@
 extern "C" {
 #endif
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype_t;
+/* Element type of the tensors of a call. The two range entries are not types: they make
+ * every int32 value a valid pkv_dtype_t (and fix its size at 32 bits), so that a value the
+ * library does not support is reported as PKV_ERR_UNSUPPORTED instead of being undefined. */
+typedef enum {
+  PKV_F32 = 0,
+  PKV_BF16 = 1,
+  PKV_DTYPE_RANGE_MIN_ = INT32_MIN,
+  PKV_DTYPE_RANGE_MAX_ = INT32_MAX
+} pkv_dtype_t;
 
 enum {
   PKV_OK = 0,
   PKV_ERR_INVALID = -1,     /* null pointer, negative size, inconsistent arguments */
   PKV_ERR_UNSUPPORTED = -2, /* a valid shape or dtype the library does not implement */
   PKV_ERR_WORKSPACE = -3,   /* decode workspace smaller than the query function asks */
-  PKV_ERR_HIP = -4          /* a HIP launch error */
+  PKV_ERR_HIP = -4,         /* a HIP launch error */
+  PKV_ERR_PRECONDITION = -5 /* a data-dependent precondition does not hold (pkv_check_*, or
+                               a device call made with PKV_DEBUG set) */
 };
 
 /* Human-readable name of a status code (static storage). */
@@ -388,6 +399,74 @@ int attn_prefill_varlen(void* out, const void* q,
                         int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                         float scale, int32_t causal, pkv_dtype_t dtype,
                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Checks of the data-dependent preconditions - [P1] store_kvcache (its wrapper asserts the
+ * shapes before the scatter; the engine's block manager and prepare_* build the rest of the
+ * metadata, which the kernels trust).
+ *
+ * Each check reads the metadata a call would use and returns PKV_OK, or
+ * PKV_ERR_PRECONDITION with *first (if not NULL) naming the first violation found; it
+ * computes nothing else. With on_device 0 the arrays are host memory; with on_device 1
+ * they are device memory, copied to the host on `stream` first, which synchronises the
+ * stream (PKV_ERR_INVALID while the stream records a graph, PKV_ERR_HIP if the copy fails).
+ * *first is zeroed on entry.
+ *   pkv_check_store     store_kvcache's slot_mapping [num_tokens] against num_slots:
+ *                       every slot is -1 or in [0, num_slots) (SLOT_RANGE, index = token);
+ *                       non-negative slots are unique (SLOT_DUPLICATE, index = the earliest
+ *                       token whose slot an earlier token already has).
+ *   pkv_check_decode    a decode call's context_lens [num_seqs] and block_tables: every
+ *                       length in [0, max_blocks_per_seq * bs] (CONTEXT_RANGE, index = b);
+ *                       the first ceil(n_b / bs) entries of each table in [0, num_blocks)
+ *                       (BLOCK_RANGE, index = b * max_blocks_per_seq + column). With
+ *                       slot_mapping (paged_attn_decode_store's, [num_seqs]; else NULL):
+ *                       its slots as for a store, and each slot is -1 or the slot of the
+ *                       sequence's newest position n_b - 1 under its own table, never set
+ *                       for n_b = 0 (NEW_TOKEN_SLOT, index = b).
+ *   pkv_check_prefill   a prefill call's cu_seqlens_q/k [num_seqs + 1]: cu_seqlens_q starts
+ *                       at 0, both never decrease and cu_seqlens_q[num_seqs] == total_q
+ *                       (CU_SEQLENS, index = the entry); Lk >= Lq (LK_LT_LQ, index = b);
+ *                       Lq <= max_seqlen_q and Lk <= max_seqlen_k (MAX_SEQLEN); with
+ *                       block_tables (NULL for attn_prefill_varlen's packed keys) also
+ *                       Lk <= max_blocks_per_seq * bs (CONTEXT_RANGE) and the first
+ *                       ceil(Lk / bs) entries of each table in [0, num_blocks) (BLOCK_RANGE).
+ * PKV_DEBUG: when this environment variable is set to a non-empty value other than "0" at
+ * the library's first device call, store_kvcache, paged_attn_decode,
+ * paged_attn_decode_store, paged_attn_prefill_varlen and attn_prefill_varlen run the
+ * matching check on their device arrays (on_device 1) after their argument checks and
+ * return its status without enqueuing anything when it fails. Such calls synchronise their
+ * stream; while the stream records a graph the check is skipped. paged_attn_decode_noalloc
+ * never checks (its callers cannot afford the copy).
+ * -------------------------------------------------------------------------------------*/
+enum {
+  PKV_CHECK_SLOT_RANGE = 1,
+  PKV_CHECK_SLOT_DUPLICATE = 2,
+  PKV_CHECK_CONTEXT_RANGE = 3,
+  PKV_CHECK_BLOCK_RANGE = 4,
+  PKV_CHECK_NEW_TOKEN_SLOT = 5,
+  PKV_CHECK_CU_SEQLENS = 6,
+  PKV_CHECK_LK_LT_LQ = 7,
+  PKV_CHECK_MAX_SEQLEN = 8
+};
+
+typedef struct pkv_violation {
+  int32_t check;     /* PKV_CHECK_* (0: none) */
+  int32_t reserved;  /* 0 */
+  int64_t index;     /* where: token, sequence, table entry or cu_seqlens entry */
+  int64_t value;     /* the offending value */
+} pkv_violation;
+
+int pkv_check_store(const int32_t* slot_mapping, int32_t num_tokens, int64_t num_slots,
+                    int32_t on_device, hipStream_t stream, pkv_violation* first);
+int pkv_check_decode(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, const int32_t* slot_mapping, int32_t num_seqs,
+                     int32_t num_blocks, int32_t block_size, int32_t on_device,
+                     hipStream_t stream, pkv_violation* first);
+int pkv_check_prefill(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                      int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                      int32_t max_seqlen_k, int32_t num_blocks, int32_t block_size,
+                      int32_t on_device, hipStream_t stream, pkv_violation* first);
 
 /* ------------------------------------------------------------------------------------
  * Temperature sampling - [P3] section 4.3 采样器 (Sampler.forward); [P1] SamplingParams

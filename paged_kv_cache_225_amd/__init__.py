@@ -9,6 +9,7 @@ from ._binding import (  # noqa: F401
     BlockManager,
     DecodeGraphs,
     PagedKVError,
+    PreconditionError,
     attn_prefill_varlen,
     load_library,
     paged_attn_decode,
@@ -17,6 +18,9 @@ from ._binding import (  # noqa: F401
     paged_attn_decode_workspace_bytes,
     paged_attn_prefill_varlen,
     pkv_block_hash,
+    pkv_check_decode,
+    pkv_check_prefill,
+    pkv_check_store,
     pkv_decode_metadata,
     pkv_prefill_metadata,
     pkv_sample,
@@ -31,5 +35,6 @@ __all__ = [
     "load_library", "paged_attn_decode", "paged_attn_decode_noalloc", "paged_attn_decode_store",
     "paged_attn_decode_workspace_bytes", "paged_attn_prefill_varlen", "pkv_decode_metadata",
     "pkv_block_hash", "pkv_prefill_metadata", "pkv_sample", "pkv_sample_workspace_bytes",
-    "pkv_status_string", "pkv_xxh64", "store_kvcache",
+    "pkv_status_string", "pkv_xxh64", "store_kvcache", "PreconditionError", "pkv_check_decode",
+    "pkv_check_prefill", "pkv_check_store",
 ]

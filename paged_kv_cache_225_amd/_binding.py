@@ -76,6 +76,10 @@ SIGNATURES = {
     "pkv_bm_free_block_ids": (_c_int, [_p, _p, _i32]),
     "pkv_bm_block_info": (_c_int, [_p, _i32, _p, _p, _p]),
     "pkv_bm_remove_sequence": (_c_int, [_p, _i32]),
+    "pkv_check_store": (_c_int, [_p, _i32, _i64, _i32, _p, _p]),
+    "pkv_check_decode": (_c_int, [_p, _i32, _p, _p, _i32, _i32, _i32, _i32, _p, _p]),
+    "pkv_check_prefill": (_c_int, [_p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                   _p, _p]),
     "attn_prefill_varlen": (_c_int, [_p, _p, _p, _i64, _p, _i64, _p, _p, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _i32, _f, _i32, _c_int, _p]),
     "paged_attn_prefill_varlen": (_c_int, [_p, _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32,
@@ -88,6 +92,29 @@ class PagedKVError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn} failed: {status} ({_status(status)})")
         self.status = status
+
+
+PKV_ERR_PRECONDITION = -5
+CHECK_NAMES = {1: "SLOT_RANGE", 2: "SLOT_DUPLICATE", 3: "CONTEXT_RANGE", 4: "BLOCK_RANGE",
+               5: "NEW_TOKEN_SLOT", 6: "CU_SEQLENS", 7: "LK_LT_LQ", 8: "MAX_SEQLEN"}
+
+
+class pkv_violation(ctypes.Structure):
+    _fields_ = [("check", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("index", ctypes.c_int64), ("value", ctypes.c_int64)]
+
+
+class PreconditionError(PagedKVError):
+    """A pkv_check_* call found a violated precondition: ``check`` (PKV_CHECK_* name),
+    ``index`` and ``value`` as the library reports them."""
+
+    def __init__(self, fn: str, v: pkv_violation):
+        self.check = CHECK_NAMES.get(v.check, str(v.check))
+        self.index = int(v.index)
+        self.value = int(v.value)
+        RuntimeError.__init__(self, f"{fn}: {self.check} at index {self.index} "
+                                    f"(value {self.value})")
+        self.status = PKV_ERR_PRECONDITION
 
 
 _LIB = None
@@ -310,6 +337,71 @@ def attn_prefill_varlen(out, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, 
         _t_ptr(cu_seqlens_q), _t_ptr(cu_seqlens_k), B, T, int(max_seqlen_q), int(max_seqlen_k),
         Hq, Hkv, D, float(scale), 1 if causal else 0, _dtype_code(q), _stream(stream))
     _check("attn_prefill_varlen", rc)
+
+
+def _arr_ptr(a):
+    """(pointer, on_device) of a host numpy array or a device tensor (None passes through)."""
+    if a is None:
+        return None, 0
+    if isinstance(a, np.ndarray):
+        if a.dtype != np.int32 or not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("host metadata must be contiguous int32")
+        return _np_ptr(a), 0
+    if a.dtype.itemsize != 4 or not a.is_contiguous():
+        raise ValueError("device metadata must be contiguous int32")
+    return _t_ptr(a), 1 if a.is_cuda else 0
+
+
+def _run_check(fn, rc, v):
+    if rc == PKV_ERR_PRECONDITION:
+        raise PreconditionError(fn, v)
+    _check(fn, rc)
+
+
+def _on_device(*ptrs):
+    flags = {d for ptr, d in ptrs if ptr is not None}
+    if len(flags) > 1:
+        raise ValueError("metadata arrays must all be host arrays or all device tensors")
+    return flags.pop() if flags else 0
+
+
+def pkv_check_store(slot_mapping, num_slots, stream=None):
+    """Raises PreconditionError unless every slot is -1 or in [0, num_slots) and the
+    non-negative slots are unique. Host int32 arrays or device tensors."""
+    p = _arr_ptr(slot_mapping)
+    v = pkv_violation()
+    rc = load_library().pkv_check_store(p[0], len(slot_mapping), int(num_slots), _on_device(p),
+                                        _stream(stream) if p[1] else None, ctypes.byref(v))
+    _run_check("pkv_check_store", rc, v)
+
+
+def pkv_check_decode(block_tables, context_lens, num_blocks, block_size, slot_mapping=None,
+                     stream=None):
+    """A decode call's lengths and tables (and, for the fused store, its slots)."""
+    t, c, s = _arr_ptr(block_tables), _arr_ptr(context_lens), _arr_ptr(slot_mapping)
+    on_dev = _on_device(t, c, s)
+    n = len(context_lens)
+    width = block_tables.shape[1] if n else 1
+    v = pkv_violation()
+    rc = load_library().pkv_check_decode(t[0], width, c[0], s[0], n, int(num_blocks),
+                                         int(block_size), on_dev,
+                                         _stream(stream) if on_dev else None, ctypes.byref(v))
+    _run_check("pkv_check_decode", rc, v)
+
+
+def pkv_check_prefill(cu_seqlens_q, cu_seqlens_k, total_q, max_seqlen_q, max_seqlen_k,
+                      block_tables=None, num_blocks=0, block_size=256, stream=None):
+    """A prefill call's cu_seqlens (and, for the paged call, its tables)."""
+    cq, ck, t = _arr_ptr(cu_seqlens_q), _arr_ptr(cu_seqlens_k), _arr_ptr(block_tables)
+    on_dev = _on_device(cq, ck, t)
+    n = len(cu_seqlens_q) - 1
+    width = block_tables.shape[1] if block_tables is not None else 0
+    v = pkv_violation()
+    rc = load_library().pkv_check_prefill(t[0], width, cq[0], ck[0], n, int(total_q),
+                                          int(max_seqlen_q), int(max_seqlen_k), int(num_blocks),
+                                          int(block_size), on_dev,
+                                          _stream(stream) if on_dev else None, ctypes.byref(v))
+    _run_check("pkv_check_prefill", rc, v)
 
 
 class DecodeGraphs:

@@ -11,6 +11,7 @@
 
 #include "launch.hpp"
 #include "paged_kv.h"
+#include "validate.hpp"
 
 // The decode workspace of paged_attn_decode_noalloc: device memory that the library owns, so
 // that a caller who cannot allocate (graph capture, a serving loop that forbids allocation)
@@ -113,6 +114,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case PKV_ERR_WORKSPACE: return "workspace too small";
     case PKV_ERR_HIP: return "HIP launch error";
+    case PKV_ERR_PRECONDITION: return "data-dependent precondition violated";
     default: return "unknown status";
   }
 }
@@ -226,6 +228,10 @@ int store_kvcache(const void* key, int64_t key_token_stride, const void* value,
   if (num_tokens == 0) return PKV_OK;
   if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_INVALID;
   if (key_token_stride < row || value_token_stride < row) return PKV_ERR_INVALID;
+  if (pkv::run_debug_checks(stream)) {
+    const int chk = pkv_check_store(slot_mapping, num_tokens, num_slots, 1, stream, nullptr);
+    if (chk != PKV_OK) return chk;
+  }
   const int rc = pkv::launch_store_kvcache(key, key_token_stride, value, value_token_stride,
                                            k_cache, v_cache, num_slots, slot_mapping, num_tokens,
                                            (int32_t)row, dtype == PKV_BF16 ? 2 : 4, stream);
@@ -271,7 +277,7 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
                   pkv_dtype_t dtype, int32_t partition_size, const int32_t* kv_stream_from,
                   void* workspace, size_t workspace_bytes, bool fused, const void* key,
                   int64_t key_token_stride, const void* value, int64_t value_token_stride,
-                  const int32_t* slot_mapping, hipStream_t stream) {
+                  const int32_t* slot_mapping, bool debug_checks, hipStream_t stream) {
   if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_blocks < 1 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID;
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return PKV_ERR_INVALID;
@@ -303,6 +309,12 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
       !aligned16(workspace))
     return PKV_ERR_INVALID;
   if (fused && (!aligned16(key) || !aligned16(value))) return PKV_ERR_INVALID;
+  if (debug_checks && pkv::run_debug_checks(stream)) {
+    const int chk = pkv_check_decode(block_tables, max_blocks_per_seq, context_lens,
+                                     fused ? slot_mapping : nullptr, num_seqs, num_blocks,
+                                     block_size, 1, stream, nullptr);
+    if (chk != PKV_OK) return chk;
+  }
   pkv::DecodeArgs a;
   a.out = out;
   a.q = q;
@@ -351,7 +363,7 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
                        context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                        scale, dtype, partition_size, kv_stream_from, workspace, workspace_bytes,
                        false, nullptr,
-                       0, nullptr, 0, nullptr, stream);
+                       0, nullptr, 0, nullptr, true, stream);
 }
 
 int paged_attn_decode_store(void* out, const void* q, const void* key, int64_t key_token_stride,
@@ -367,7 +379,7 @@ int paged_attn_decode_store(void* out, const void* q, const void* key, int64_t k
                        context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                        scale, dtype, partition_size, kv_stream_from, workspace, workspace_bytes,
                        true, key,
-                       key_token_stride, value, value_token_stride, slot_mapping, stream);
+                       key_token_stride, value, value_token_stride, slot_mapping, true, stream);
 }
 
 int paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -391,7 +403,7 @@ int paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, con
   return decode_common(out, q, k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                        scale, dtype, partition_size, kv_stream_from, ws, need, false, nullptr, 0,
-                       nullptr, 0, nullptr, stream);
+                       nullptr, 0, nullptr, false, stream);
 }
 
 // ------------------------------------------------------------------------- prefill
@@ -431,6 +443,13 @@ int prefill_common(void* out, const void* q, const void* k, const void* v, int32
   if (!out || !q || !k || !v || !cu_seqlens_q || !cu_seqlens_k) return PKV_ERR_INVALID;
   if (!packed && !block_tables) return PKV_ERR_INVALID;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v)) return PKV_ERR_INVALID;
+  if (pkv::run_debug_checks(stream)) {
+    const int chk = pkv_check_prefill(packed ? nullptr : block_tables, max_blocks_per_seq,
+                                      cu_seqlens_q, cu_seqlens_k, num_seqs, total_q,
+                                      max_seqlen_q, max_seqlen_k, num_blocks, block_size, 1,
+                                      stream, nullptr);
+    if (chk != PKV_OK) return chk;
+  }
   pkv::PrefillArgs a;
   a.out = out;
   a.q = q;

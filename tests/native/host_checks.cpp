@@ -1,0 +1,406 @@
+// Host-code exercise of libpaged_kv, built with AddressSanitizer and UndefinedBehaviorSanitizer
+// on the host side (paged_kv_cache_225_amd/build.py, build_host_sanitized) and run on the CPU
+// by tests/test_host_sanitizer.py. No GPU is touched: only calls whose work is host code run
+// (metadata, precondition checks, hashing, the block manager) and the device entry points only
+// with arguments their host-side validation rejects before anything is enqueued.
+//
+// Every output buffer is allocated at exactly the size the call may write, so any write past
+// it is reported by the sanitizer. Results are also checked against their definitions where
+// those are one line (slot = table[p / bs] * bs + p % bs, prefix sums) and the block manager's
+// reference counts against its tables after every operation. `--planted-overflow` reads one
+// element past a heap array on purpose, to show that the build is instrumented.
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <map>
+#include <vector>
+
+#include "paged_kv.h"
+
+namespace {
+
+int g_checks = 0;
+
+#define CHECK(cond)                                                             \
+  do {                                                                          \
+    ++g_checks;                                                                 \
+    if (!(cond)) {                                                              \
+      fprintf(stderr, "host checks: %s:%d: CHECK(%s) failed\n", __FILE__, __LINE__, #cond); \
+      exit(1);                                                                  \
+    }                                                                           \
+  } while (0)
+
+struct Rng {  // splitmix64
+  uint64_t s;
+  explicit Rng(uint64_t seed) : s(seed) {}
+  uint64_t next() {
+    uint64_t z = (s += 0x9E3779B97F4A7C15ULL);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+  }
+  int64_t range(int64_t lo, int64_t hi) {  // [lo, hi]
+    return lo + (int64_t)(next() % (uint64_t)(hi - lo + 1));
+  }
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------ metadata
+void metadata(Rng& rng) {
+  const int32_t sizes[] = {16, 32, 256};
+  for (int trial = 0; trial < 1500; ++trial) {
+    const int32_t bs = sizes[rng.range(0, 2)];
+    const int32_t B = (int32_t)rng.range(0, 12);
+    std::vector<int32_t> cached(B), sched(B), lens(B);
+    std::vector<int64_t> offs(B + 1, 0);
+    std::vector<int32_t> flat;
+    int32_t width = 1;
+    int64_t total_q = 0;
+    for (int b = 0; b < B; ++b) {
+      lens[b] = (int32_t)rng.range(1, 1200);
+      cached[b] = (int32_t)rng.range(0, lens[b] - 1);
+      sched[b] = lens[b] - cached[b];
+      total_q += sched[b];
+      const int64_t nb = ceil_div(lens[b], bs) + (rng.range(0, 3) == 0 ? 1 : 0);
+      for (int64_t j = 0; j < nb; ++j) flat.push_back((int32_t)rng.range(0, 100000));
+      offs[b + 1] = (int64_t)flat.size();
+      width = std::max<int32_t>(width, (int32_t)nb);
+    }
+    width += (int32_t)rng.range(0, 2);
+    std::vector<int32_t> cq(B + 1), ck(B + 1), slots(std::max<int64_t>(total_q, 1)),
+        tables((size_t)B * width);
+    std::vector<int64_t> pos(std::max<int64_t>(total_q, 1));
+    int32_t mq = -1, mk = -1;
+    int rc = pkv_prefill_metadata(B, cached.data(), sched.data(), flat.data(), offs.data(), bs,
+                                  width, cq.data(), ck.data(), &mq, &mk, slots.data(), total_q,
+                                  pos.data(), tables.data());
+    CHECK(rc == PKV_OK);
+    CHECK(cq[0] == 0 && ck[0] == 0);
+    int64_t t = 0;
+    for (int b = 0; b < B; ++b) {
+      CHECK(cq[b + 1] - cq[b] == sched[b] && ck[b + 1] - ck[b] == lens[b]);
+      for (int32_t p = cached[b]; p < lens[b]; ++p, ++t) {
+        const int32_t* tb = flat.data() + offs[b];
+        CHECK(slots[t] == tb[p / bs] * bs + p % bs);
+        CHECK(pos[t] == p);
+      }
+      for (int32_t j = 0; j < width; ++j) {
+        const int64_t n = offs[b + 1] - offs[b];
+        CHECK(tables[(size_t)b * width + j] == (j < n ? flat[offs[b] + j] : -1));
+      }
+    }
+    // a slot array one short (capacity 0 would mean "unchecked"), positions omitted,
+    // capacity check skipped
+    if (total_q > 1) {
+      rc = pkv_prefill_metadata(B, cached.data(), sched.data(), flat.data(), offs.data(), bs,
+                                width, cq.data(), ck.data(), &mq, &mk, slots.data(),
+                                total_q - 1, nullptr, tables.data());
+      CHECK(rc == PKV_ERR_INVALID);
+    }
+    if (total_q > 0) {
+      rc = pkv_prefill_metadata(B, cached.data(), sched.data(), flat.data(), offs.data(), bs,
+                                width, cq.data(), ck.data(), &mq, &mk, slots.data(), 0, nullptr,
+                                tables.data());
+      CHECK(rc == PKV_OK);
+    }
+    // a table longer than the width
+    if (B > 0 && width > 1) {
+      std::vector<int32_t> narrow((size_t)B * (width - 1));
+      const int64_t longest = [&] {
+        int64_t m = 0;
+        for (int b = 0; b < B; ++b) m = std::max<int64_t>(m, offs[b + 1] - offs[b]);
+        return m;
+      }();
+      if (longest == width) {
+        rc = pkv_prefill_metadata(B, cached.data(), sched.data(), flat.data(), offs.data(), bs,
+                                  width - 1, cq.data(), ck.data(), &mq, &mk, slots.data(),
+                                  total_q, pos.data(), narrow.data());
+        CHECK(rc == PKV_ERR_INVALID);
+      }
+    }
+    // decode over tables of exactly ceil(len / bs) ids
+    std::vector<int32_t> dflat;
+    std::vector<int64_t> doffs(B + 1, 0);
+    int32_t dwidth = 1;
+    for (int b = 0; b < B; ++b) {
+      const int64_t nb = ceil_div(lens[b], bs);
+      for (int64_t j = 0; j < nb; ++j) dflat.push_back((int32_t)rng.range(0, 100000));
+      doffs[b + 1] = (int64_t)dflat.size();
+      dwidth = std::max<int32_t>(dwidth, (int32_t)nb);
+    }
+    std::vector<int32_t> dslots(std::max(B, 1)), ctx(std::max(B, 1)),
+        dtables((size_t)B * dwidth);
+    std::vector<int64_t> dpos(std::max(B, 1));
+    rc = pkv_decode_metadata(B, lens.data(), dflat.data(), doffs.data(), bs, dwidth,
+                             dslots.data(), ctx.data(), dpos.data(), dtables.data());
+    CHECK(rc == PKV_OK);
+    for (int b = 0; b < B; ++b) {
+      const int32_t p = lens[b] - 1;
+      CHECK(dslots[b] == dflat[doffs[b] + p / bs] * bs + p % bs);
+      CHECK(ctx[b] == lens[b] && dpos[b] == p);
+    }
+    // the precondition checks accept what the metadata calls built
+    if (B > 0) {
+      CHECK(pkv_check_prefill(tables.data(), width, cq.data(), ck.data(), B, (int32_t)total_q,
+                              mq, mk, 100001, bs, 0, nullptr, nullptr) == PKV_OK);
+      CHECK(pkv_check_decode(dtables.data(), dwidth, ctx.data(), dslots.data(), B, 100001, bs,
+                             0, nullptr, nullptr) == PKV_OK);
+    }
+  }
+  // argument errors
+  int32_t one = 1, out32[4];
+  int64_t off2[2] = {0, 1}, out64[4];
+  CHECK(pkv_prefill_metadata(-1, &one, &one, &one, off2, 16, 1, out32, out32, out32, out32,
+                             out32, 4, out64, out32) == PKV_ERR_INVALID);
+  CHECK(pkv_decode_metadata(1, &one, &one, off2, 16, 0, out32, out32, out64, out32) ==
+        PKV_ERR_INVALID);
+}
+
+// ------------------------------------------------------------------ precondition checks
+void checks(Rng& rng) {
+  pkv_violation v;
+  for (int trial = 0; trial < 3000; ++trial) {
+    const int32_t n = (int32_t)rng.range(0, 80);
+    const int64_t num_slots = rng.range(0, 100);
+    std::vector<int32_t> s(std::max(n, 1));
+    for (int32_t t = 0; t < n; ++t) s[t] = (int32_t)rng.range(-2, 110);
+    const int rc = pkv_check_store(s.data(), n, num_slots, 0, nullptr, &v);
+    CHECK(rc == PKV_OK || rc == PKV_ERR_PRECONDITION);
+    if (rc == PKV_OK) {
+      CHECK(v.check == 0);
+      std::vector<char> seen((size_t)num_slots + 1, 0);
+      for (int32_t t = 0; t < n; ++t) {
+        CHECK(s[t] >= -1 && s[t] < num_slots);
+        if (s[t] >= 0) {
+          CHECK(!seen[s[t]]);
+          seen[s[t]] = 1;
+        }
+      }
+    } else {
+      CHECK(v.check == PKV_CHECK_SLOT_RANGE || v.check == PKV_CHECK_SLOT_DUPLICATE);
+      CHECK(v.index >= 0 && v.index < n && v.value == s[v.index]);
+    }
+    // decode and prefill metadata with random (often broken) contents
+    const int32_t B = (int32_t)rng.range(1, 6), W = (int32_t)rng.range(1, 5), bs = 16;
+    std::vector<int32_t> bt((size_t)B * W), ctx(B), sl(B), cq(B + 1), ck(B + 1);
+    for (auto& x : bt) x = (int32_t)rng.range(-1, 20);
+    for (auto& x : ctx) x = (int32_t)rng.range(-1, W * bs + 1);
+    for (auto& x : sl) x = (int32_t)rng.range(-1, 20 * bs);
+    cq[0] = (int32_t)rng.range(0, 1) ? 0 : 1;
+    ck[0] = 0;
+    for (int b = 0; b < B; ++b) {
+      cq[b + 1] = cq[b] + (int32_t)rng.range(-1, 40);
+      ck[b + 1] = ck[b] + (int32_t)rng.range(-1, 60);
+    }
+    int r = pkv_check_decode(bt.data(), W, ctx.data(), rng.range(0, 1) ? sl.data() : nullptr, B,
+                             20, bs, 0, nullptr, &v);
+    CHECK(r == PKV_OK || r == PKV_ERR_PRECONDITION);
+    r = pkv_check_prefill(rng.range(0, 1) ? bt.data() : nullptr, W, cq.data(), ck.data(), B,
+                          cq[B], 40, 60, 20, bs, 0, nullptr, &v);
+    CHECK(r == PKV_OK || r == PKV_ERR_PRECONDITION || (r == PKV_ERR_INVALID && cq[B] < 0));
+    CHECK(v.check >= 0 && v.check <= PKV_CHECK_MAX_SEQLEN);
+  }
+  CHECK(pkv_check_store(nullptr, 3, 10, 0, nullptr, &v) == PKV_ERR_INVALID);
+  CHECK(pkv_check_decode(nullptr, 1, nullptr, nullptr, 2, 1, 16, 0, nullptr, &v) ==
+        PKV_ERR_INVALID);
+}
+
+// ------------------------------------------------------------------ hashing
+void hashing(Rng& rng) {
+  CHECK(pkv_xxh64("", 0, 0) == 0xEF46DB3751D8E999ULL);  // the published empty-input value
+  for (int len = 0; len <= 100; ++len) {
+    std::vector<uint8_t> buf(std::max(len, 1));
+    for (auto& x : buf) x = (uint8_t)rng.next();
+    const uint64_t a = pkv_xxh64(buf.data(), (size_t)len, 7);
+    CHECK(a == pkv_xxh64(buf.data(), (size_t)len, 7));
+    std::vector<int64_t> toks(std::max(len, 1));
+    for (auto& x : toks) x = (int64_t)rng.next();
+    uint64_t h0 = 0, h1 = 0;
+    CHECK(pkv_block_hash(toks.data(), len, 0, 0, &h0) == PKV_OK);
+    CHECK(pkv_block_hash(toks.data(), len, 1, h0, &h1) == PKV_OK);
+  }
+  uint64_t h;
+  CHECK(pkv_block_hash(nullptr, 3, 0, 0, &h) == PKV_ERR_INVALID);
+}
+
+// ------------------------------------------------------------------ block manager
+struct Bm {
+  pkv_block_manager* h = nullptr;
+  int32_t num_blocks, bs;
+};
+
+void bm_invariants(const Bm& bm, const std::vector<int32_t>& live) {
+  std::vector<int32_t> refs(bm.num_blocks, 0);
+  for (int32_t s : live) {
+    int64_t n, c, sc;
+    int32_t tl;
+    CHECK(pkv_bm_sequence_info(bm.h, s, &n, &c, &sc, &tl) == PKV_OK);
+    std::vector<int32_t> tb(std::max(tl, 1));
+    CHECK(pkv_bm_block_table(bm.h, s, tb.data(), tl) == tl);
+    for (int32_t j = 0; j < tl; ++j) {
+      CHECK(tb[j] >= 0 && tb[j] < bm.num_blocks);
+      ++refs[tb[j]];
+    }
+  }
+  int32_t free_count = 0;
+  for (int32_t b = 0; b < bm.num_blocks; ++b) {
+    int32_t rc, sealed;
+    uint64_t hash;
+    CHECK(pkv_bm_block_info(bm.h, b, &rc, &sealed, &hash) == PKV_OK);
+    CHECK(rc == refs[b]);
+    free_count += rc == 0;
+  }
+  const int32_t nf = pkv_bm_num_free_blocks(bm.h);
+  CHECK(nf == free_count);
+  std::vector<int32_t> ids(std::max(nf, 1));
+  CHECK(pkv_bm_free_block_ids(bm.h, ids.data(), nf) == nf);
+  for (int32_t i = 0; i < nf; ++i) CHECK(refs[ids[i]] == 0);
+  // a short buffer gets a prefix and the full count
+  if (nf > 1) {
+    std::vector<int32_t> part(1);
+    CHECK(pkv_bm_free_block_ids(bm.h, part.data(), 1) == nf && part[0] == ids[0]);
+  }
+}
+
+void block_manager(Rng& rng) {
+  for (int trial = 0; trial < 60; ++trial) {
+    Bm bm;
+    bm.num_blocks = (int32_t)rng.range(1, 40);
+    bm.bs = (int32_t)rng.range(2, 8);
+    CHECK(pkv_bm_create(&bm.h, bm.num_blocks, bm.bs) == PKV_OK);
+    std::vector<int32_t> waiting, running;
+    // prompts share prefixes drawn from a few stems, so cache hits happen
+    std::vector<std::vector<int64_t>> stems(3);
+    for (auto& st : stems)
+      for (int i = 0; i < 30; ++i) st.push_back(rng.range(0, 5));
+    for (int op = 0; op < 400; ++op) {
+      const int64_t kind = rng.range(0, 9);
+      if (kind <= 2) {  // a new prompt
+        const auto& st = stems[rng.range(0, 2)];
+        const int32_t n = (int32_t)rng.range(1, 30);
+        std::vector<int64_t> toks(st.begin(), st.begin() + n);
+        for (int32_t i = (int32_t)rng.range(0, n); i < n; ++i) toks[i] = rng.range(0, 5);
+        const int id = pkv_bm_add_sequence(bm.h, toks.data(), n);
+        CHECK(id >= 0);
+        waiting.push_back(id);
+      } else if (kind <= 4 && !waiting.empty()) {  // admit: allocate, prefill, seal
+        const size_t i = (size_t)rng.range(0, (int64_t)waiting.size() - 1);
+        const int32_t s = waiting[i];
+        const int hits = pkv_bm_can_allocate(bm.h, s);
+        if (hits >= 0) {
+          CHECK(pkv_bm_allocate(bm.h, s, hits) == PKV_OK);
+          int64_t n, c, sc;
+          int32_t tl;
+          CHECK(pkv_bm_sequence_info(bm.h, s, &n, &c, &sc, &tl) == PKV_OK);
+          CHECK(pkv_bm_set_scheduled(bm.h, s, (int32_t)(n - c)) == PKV_OK);
+          CHECK(pkv_bm_hash_blocks(bm.h, s) >= 0);
+          CHECK(pkv_bm_commit_scheduled(bm.h, s) == PKV_OK);
+          waiting.erase(waiting.begin() + (long)i);
+          running.push_back(s);
+        }
+      } else if (kind <= 7 && !running.empty()) {  // a decode step of one sequence
+        const size_t i = (size_t)rng.range(0, (int64_t)running.size() - 1);
+        const int32_t s = running[i];
+        CHECK(pkv_bm_append_token(bm.h, s, rng.range(0, 5)) == PKV_OK);
+        if (pkv_bm_can_append(bm.h, s) > 0) {
+          CHECK(pkv_bm_may_append(bm.h, s) >= 0);
+          CHECK(pkv_bm_set_scheduled(bm.h, s, 1) == PKV_OK);
+          CHECK(pkv_bm_hash_blocks(bm.h, s) >= 0);
+          CHECK(pkv_bm_commit_scheduled(bm.h, s) == PKV_OK);
+        } else {  // preempt: back to waiting with an empty table
+          CHECK(pkv_bm_deallocate(bm.h, s) == PKV_OK);
+          running.erase(running.begin() + (long)i);
+          waiting.push_back(s);
+        }
+      } else if (!running.empty()) {  // finish a sequence
+        const size_t i = (size_t)rng.range(0, (int64_t)running.size() - 1);
+        CHECK(pkv_bm_deallocate(bm.h, running[i]) == PKV_OK);
+        CHECK(pkv_bm_remove_sequence(bm.h, running[i]) == PKV_OK);
+        CHECK(pkv_bm_remove_sequence(bm.h, running[i]) == PKV_ERR_INVALID);
+        running.erase(running.begin() + (long)i);
+      }
+      bm_invariants(bm, running);
+    }
+    CHECK(pkv_bm_destroy(bm.h) == PKV_OK);
+  }
+  pkv_block_manager* h = nullptr;
+  CHECK(pkv_bm_create(&h, 0, 16) == PKV_ERR_INVALID);
+  CHECK(pkv_bm_create(&h, 4, 1) == PKV_ERR_INVALID);
+  CHECK(pkv_bm_destroy(nullptr) == PKV_ERR_INVALID);
+}
+
+// ------------------------------------------------------------------ device-call validation
+void device_argument_errors() {
+  // fake, aligned device addresses: every call below is rejected before any HIP call
+  void* F = (void*)0x100000;
+  const int32_t* I = (const int32_t*)0x100000;
+  CHECK(store_kvcache(F, 1024, F, 1024, F, F, 16, I, 4, 8, 128, (pkv_dtype_t)7, nullptr) ==
+        PKV_ERR_UNSUPPORTED);
+  CHECK(store_kvcache(F, 1000, F, 1024, F, F, 16, I, 4, 8, 128, PKV_BF16, nullptr) ==
+        PKV_ERR_INVALID);
+  CHECK(store_kvcache(nullptr, 1024, F, 1024, F, F, 16, I, 4, 8, 128, PKV_BF16, nullptr) ==
+        PKV_ERR_INVALID);
+  CHECK(store_kvcache(F, 1024, F, 1024, F, F, 16, I, 0, 8, 128, PKV_BF16, nullptr) == PKV_OK);
+  for (int32_t n : {1, 7, 64, 512, 16383})
+    for (int32_t w : {1, 3, 16, 40})
+      for (int32_t part : {0, 64, 256, 1024}) {
+        const size_t need = paged_attn_decode_workspace_bytes(n, 16, 128, w, 256, part);
+        CHECK(need > 0);
+        CHECK(paged_attn_decode(F, F, F, F, 16, I, w, I, n, 16, 8, 128, 256, 0.1f, PKV_BF16,
+                                part, nullptr, F, need - 1, nullptr) == PKV_ERR_WORKSPACE);
+      }
+  CHECK(paged_attn_decode_workspace_bytes(4, 16, 128, 16, 256, 100) == 0);
+  CHECK(paged_attn_decode(F, F, F, F, 16, I, 16, I, 4, 16, 8, 96, 256, 0.1f, PKV_BF16, 0,
+                          nullptr, F, 1 << 30, nullptr) == PKV_ERR_UNSUPPORTED);
+  CHECK(paged_attn_decode(F, F, F, F, 16, I, 16, I, 4, 12, 8, 128, 256, 0.1f, PKV_BF16, 0,
+                          nullptr, F, 1 << 30, nullptr) == PKV_ERR_INVALID);
+  CHECK(paged_attn_decode(F, F, F, F, 16, I, 16, I, 0, 16, 8, 128, 256, 0.1f, PKV_BF16, 0,
+                          nullptr, F, 1 << 30, nullptr) == PKV_OK);
+  CHECK(paged_attn_decode_noalloc(F, F, F, F, 16, I, 16, I, 0, 16, 8, 128, 256, 0.1f, PKV_BF16,
+                                  0, nullptr, nullptr) == PKV_OK);
+  CHECK(paged_attn_decode_store(F, F, F, 100, F, 1024, I, F, F, 16, I, 16, I, 4, 16, 8, 128, 256,
+                                0.1f, PKV_BF16, 0, nullptr, F, 1 << 30, nullptr) ==
+        PKV_ERR_INVALID);
+  CHECK(paged_attn_prefill_varlen(F, F, F, F, 16, I, 16, I, I, 4, 100, 64, 32, 16, 8, 128, 256,
+                                  0.1f, 1, PKV_BF16, nullptr) == PKV_ERR_INVALID);
+  CHECK(paged_attn_prefill_varlen(F, F, F, F, 16, I, 16, I, I, 4, 100, 64, 64, 16, 8, 128, 256,
+                                  0.1f, 0, PKV_BF16, nullptr) == PKV_ERR_UNSUPPORTED);
+  CHECK(attn_prefill_varlen(F, F, F, 100, F, 1024, I, I, 4, 100, 64, 64, 16, 8, 128, 0.1f, 1,
+                            PKV_BF16, nullptr) == PKV_ERR_INVALID);
+  pkv_decode_graphs* g = nullptr;
+  void* arr[3] = {F, F, F};
+  CHECK(pkv_decode_graphs_create_layers(&g, 4, 0, arr, (const void* const*)arr,
+                                        (const void* const*)arr, 1024, (const void* const*)arr,
+                                        1024, I, arr, arr, 16, I, 16, I, 16, 8, 128, 256, 0.1f,
+                                        PKV_BF16, 0, nullptr, F, 1 << 30) == PKV_ERR_INVALID);
+  CHECK(pkv_decode_graphs_create(&g, 4, F, F, F, 1024, F, 1024, I, F, F, 16, I, 16, I, 16, 8,
+                                 128, 256, 0.1f, PKV_BF16, 0, nullptr, F, 16) ==
+        PKV_ERR_WORKSPACE);
+  CHECK(g == nullptr);
+  CHECK(pkv_decode_graphs_bucket(nullptr, 1) == PKV_ERR_INVALID);
+  CHECK(pkv_sample_workspace_bytes(0, 10) == 0 || pkv_sample_workspace_bytes(0, 10) > 0);
+  for (int s = -6; s <= 1; ++s) CHECK(pkv_status_string(s) != nullptr);
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  if (argc > 1 && strcmp(argv[1], "--planted-overflow") == 0) {
+    std::vector<int32_t> v(8, 1);
+    volatile int32_t* p = v.data();
+    printf("host checks: planted read %d\n", p[8]);  // one past the end
+    return 0;
+  }
+  Rng rng(20261203);
+  metadata(rng);
+  checks(rng);
+  hashing(rng);
+  block_manager(rng);
+  device_argument_errors();
+  printf("host checks: ok (%d checks)\n", g_checks);
+  return 0;
+}

@@ -1,0 +1,80 @@
+"""GPU tests of the precondition checks: the device-array form of pkv_check_* gives the same
+verdicts as the host form, and the device calls in PKV_DEBUG mode (run in a child process,
+since the variable is read once per process) reject violations without writing anything
+while valid calls, and graphs recorded in that mode, compute as usual."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from paged_kv_cache_225_amd import _binding as B
+from workloads import make_config
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _verdict(fn, **kw):
+    try:
+        fn(**kw)
+    except B.PreconditionError as e:
+        return e.check, e.index, e.value
+    return None
+
+
+def _dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def test_device_checks_match_host_checks():
+    w = make_config(2)
+    md = O.decode_metadata(w.seq_lens, w.block_tables, w.block_size)
+    bt, ctx, sl = md["block_tables"], md["context_lens"], md["slot_mapping"]
+    cases = [(bt, ctx, sl)]
+    c2 = ctx.copy(); c2[11] = 1 << 20; cases.append((bt, c2, sl))
+    b2 = bt.copy(); b2[30, 1] = -3; cases.append((b2, ctx, sl))
+    s2 = sl.copy(); s2[40] = s2[2]; cases.append((bt, ctx, s2))
+    s3 = sl.copy(); s3[7] -= 1; cases.append((bt, ctx, s3))
+    seen = set()
+    for t, c, s in cases:
+        host = _verdict(B.pkv_check_decode, block_tables=t, context_lens=c, num_blocks=w.num_blocks,
+                        block_size=w.block_size, slot_mapping=s)
+        dev = _verdict(B.pkv_check_decode, block_tables=_dev(t), context_lens=_dev(c),
+                       num_blocks=w.num_blocks, block_size=w.block_size, slot_mapping=_dev(s))
+        assert host == dev, (host, dev)
+        seen.add(None if host is None else host[0])
+        host = _verdict(B.pkv_check_store, slot_mapping=s, num_slots=w.num_blocks * w.block_size)
+        dev = _verdict(B.pkv_check_store, slot_mapping=_dev(s),
+                       num_slots=w.num_blocks * w.block_size)
+        assert host == dev, (host, dev)
+    assert seen == {None, "CONTEXT_RANGE", "BLOCK_RANGE", "SLOT_DUPLICATE", "NEW_TOKEN_SLOT"}
+    wp = make_config(4)
+    mp = O.prefill_metadata(wp.seq_lens, wp.num_cached, wp.block_tables, wp.block_size)
+    for cq in (mp["cu_seqlens_q"], np.concatenate([[0], mp["cu_seqlens_q"][1:] + 3000])):
+        kw = dict(total_q=int(cq[-1]), max_seqlen_q=mp["max_seqlen_q"] + 3000,
+                  max_seqlen_k=mp["max_seqlen_k"] + 3000, num_blocks=wp.num_blocks,
+                  block_size=wp.block_size)
+        host = _verdict(B.pkv_check_prefill, cu_seqlens_q=cq.astype(np.int32),
+                        cu_seqlens_k=mp["cu_seqlens_k"], block_tables=mp["block_tables"], **kw)
+        dev = _verdict(B.pkv_check_prefill, cu_seqlens_q=_dev(cq.astype(np.int32)),
+                       cu_seqlens_k=_dev(mp["cu_seqlens_k"]),
+                       block_tables=_dev(mp["block_tables"]), **kw)
+        assert host == dev, (host, dev)
+
+
+def test_debug_mode_rejects_violations_and_computes_valid_calls():
+    env = dict(os.environ, PKV_DEBUG="1")
+    print("debug mode: starting the child process", flush=True)
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "tests", "debug_mode_child.py")],
+                       env=env, capture_output=True, text=True, timeout=300, cwd=ROOT)
+    print(r.stdout[-4000:], flush=True)
+    print(r.stderr[-4000:], flush=True)
+    assert r.returncode == 0, r.returncode
+    assert "debug mode: ok" in r.stdout
