@@ -405,16 +405,15 @@ __device__ __forceinline__ void bits_to_float(const typename LaneBits<T, DPL>::t
 }
 
 // Merges the partial slots of every (sequence, query head) whose segment was split: one
-// wavefront per (sequence, head), four per workgroup. The kernel is latency bound, so it
-// takes two rounds of loads: first the split metadata together with the (m, l) of the
-// first 64 slots (lane p holds slot p; the slots exist for every row, so they are read
-// before the row's slot count is known), the o rows of the first kSpec slots and, for the
-// fused store, q and the newest token's rows; then the o rows of the remaining slots, up
-// to 16 at a time, D / 64 consecutive floats per lane (one coalesced row per load
-// instruction). A row cut into at most kSpec pieces needs no second round. With FEW (a call
-// of few rows, where the grid is small and the rounds' latency is the whole cost) the first
-// round takes the o rows of the first 64 slots, so only slots past 64 need another round.
-template <typename T, int D, bool FEW>
+// wavefront per (sequence, head), four per workgroup (calls of many rows; few rows go to
+// decode_combine_wide_kernel). The kernel is latency bound, so it takes two rounds of loads:
+// first the split metadata together with the (m, l) of the first 64 slots (lane p holds slot
+// p; the slots exist for every row, so they are read before the row's slot count is known),
+// the o rows of the first kSpec slots and, for the fused store, q and the newest token's
+// rows; then the o rows of the remaining slots, up to 16 at a time, D / 64 consecutive floats
+// per lane (one coalesced row per load instruction). A row cut into at most kSpec pieces
+// needs no second round.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     T* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t cap,
     int32_t num_rows, int32_t Hq, int32_t Hkv, int32_t max_pieces,
@@ -422,7 +421,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     const int32_t* __restrict__ ws_meta, int32_t per_seq_line, NewTokens nt) {
   constexpr int DPL = D / 64;  // floats per lane
   constexpr int OB = 16;       // o rows per load batch
-  constexpr int kSpec = FEW ? 64 : 4;  // o rows loaded in the first round, before the count is known
+  constexpr int kSpec = 4;     // o rows loaded in the first round, before the count is known
   static_assert(DPL == 1 || DPL == 2, "head_dim 64 or 128");
   typedef typename LaneBits<T, DPL>::type Bits;
   const int lane = threadIdx.x & 63;
@@ -444,11 +443,6 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   float ov0[kSpec][DPL];
 #pragma unroll
   for (int u = 0; u < kSpec; ++u) {
-    if constexpr (FEW) {  // only existing slots (a uniform test; the trip count stays fixed)
-      ov0[u][0] = 0.f;
-      if constexpr (DPL == 2) ov0[u][1] = 0.f;
-      if (u >= max_pieces) continue;
-    }
     const float* src = ws_o + (base + min(u, max_pieces - 1)) * D + lane * DPL;
     if constexpr (DPL == 2) {
       const float2 v = *reinterpret_cast<const float2*>(src);
@@ -500,24 +494,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[e] *= rescale;
       M = Mn;
-      if constexpr (FEW) {
-        if (p0 == 0) {  // the first 64 slots' o rows are in ov0 already
-#pragma unroll
-          for (int u = 0; u < kSpec; ++u) {
-            if (u >= cnt) continue;
-            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wp), u));
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, ov0[u][e], acc[e]);
-          }
-          continue;
-        }
-      }
       // round 2: the o rows not loaded yet
       for (int p = 0; p < cnt; p += OB) {
         float ov[OB][DPL];
 #pragma unroll
         for (int u = 0; u < OB; ++u) {
-          if (!FEW && u < kSpec && p0 == 0 && p == 0) {
+          if (u < kSpec && p0 == 0 && p == 0) {
 #pragma unroll
             for (int e = 0; e < DPL; ++e) ov[u][e] = ov0[u < kSpec ? u : 0][e];
             continue;
@@ -579,9 +561,164 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   }
 }
 
-// Calls of at most this many (sequence, q head) rows - at most 64 combine workgroups - load
-// the first 64 slots' o rows in the combine's first round. Measured with 16 q heads: batch
-// 16 (33 slots) 1.4 us faster per call, batch 64 (1024 rows, 17 slots) 1 us slower.
+// Merges the partial slots of one (sequence, query head) per workgroup, for calls of few rows
+// (a small batch, where the merge's cost is its latency and the few workgroups of the
+// one-wavefront-per-row form leave most of the chip idle): wavefront w takes slots w*16 ..
+// w*16+15 of every 64, so one round of loads covers a row of up to 64 pieces; the four
+// wavefronts' (m, l, o) are then merged through LDS by wavefront 0, which also adds the
+// newest token (fused store) and writes the row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_combine_wide_kernel(
+    T* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t cap,
+    int32_t num_rows, int32_t Hq, int32_t Hkv, int32_t max_pieces,
+    const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
+    const int32_t* __restrict__ ws_meta, int32_t per_seq_line, NewTokens nt) {
+  constexpr int DPL = D / 64;
+  constexpr int SPW = 16;  // slots per wavefront per round
+  static_assert(DPL == 1 || DPL == 2, "head_dim 64 or 128");
+  typedef typename LaneBits<T, DPL>::type Bits;
+  __shared__ float s_part[4][2 + 64 * DPL];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x;  // b * Hq + h
+  if (row >= num_rows) return;
+  const int b = row / Hq, h = row - b * Hq;
+  const int g = h / (Hq / Hkv);
+  const int64_t base = (int64_t)row * max_pieces;
+  const bool fused = nt.key != nullptr;
+  // round 1: metadata, this wavefront's first 16 slots, and (wavefront 0) the newest token
+  const int n_raw = context_lens[b];
+  const int S = ws_meta[0];
+  const int cum = ws_meta[1 + b];
+  auto load_slots = [&](int p0, float& mp, float& lp, float (*ov)[DPL]) {
+    const int s0 = p0 + wave * SPW;
+    mp = -INFINITY;
+    lp = 0.f;
+    if (lane < SPW && s0 + lane < max_pieces) {
+      mp = ws_ml[2 * (base + s0 + lane)];
+      lp = ws_ml[2 * (base + s0 + lane) + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+      const float* src = ws_o + (base + min(s0 + u, max_pieces - 1)) * D + lane * DPL;
+      if constexpr (DPL == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(src);
+        ov[u][0] = v.x;
+        ov[u][1] = v.y;
+      } else {
+        ov[u][0] = *src;
+      }
+    }
+  };
+  float mp, lp, ov[SPW][DPL];
+  load_slots(0, mp, lp, ov);
+  Bits qw{}, kw{}, vw{};
+  int slot = -1;
+  if (fused && wave == 0) {
+    const int64_t col = (int64_t)g * D + lane * DPL;
+    qw = *reinterpret_cast<const Bits*>(reinterpret_cast<const T*>(nt.q) + (int64_t)row * D + lane * DPL);
+    kw = *reinterpret_cast<const Bits*>(reinterpret_cast<const T*>(nt.key) + b * nt.key_stride + col);
+    vw = *reinterpret_cast<const Bits*>(reinterpret_cast<const T*>(nt.value) + b * nt.value_stride + col);
+    slot = nt.slot_mapping[b];
+  }
+  const int n = clamp_ctx(n_raw, cap);
+  const int nc = fused ? n - (n > 0) : n;
+  float acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  float M = -INFINITY, L = 0.f;
+  if (nc > 0) {
+    const int seg_start = per_seq_line ? cum : Hkv * cum + g * nc;
+    const int np = (seg_start + nc - 1) / S - seg_start / S + 1;
+    if (np == 1 && !fused) return;  // written by the stream kernel (uniform over the group)
+    for (int p0 = 0; p0 < np; p0 += 4 * SPW) {
+      if (p0 > 0) load_slots(p0, mp, lp, ov);
+      const int s0 = p0 + wave * SPW;
+      const int cnt = max(0, min(SPW, np - s0));  // this wavefront's slots in the round
+      if (lane >= cnt) {
+        mp = -INFINITY;
+        lp = 0.f;
+      }
+      if (cnt == 0) continue;
+      const float Mn = fmaxf(M, group_max<64>(mp));
+      const float rescale = __builtin_amdgcn_exp2f(M - Mn);
+      const float wp = lane < cnt ? __builtin_amdgcn_exp2f(mp - Mn) : 0.f;
+      L = fmaf(L, rescale, group_sum<64>(wp * lp));
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] *= rescale;
+      M = Mn;
+#pragma unroll
+      for (int u = 0; u < SPW; ++u) {
+        if (u >= cnt) break;
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wp), u));
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, ov[u][e], acc[e]);
+      }
+    }
+  }
+  // the four wavefronts' states, merged by wavefront 0
+  if (lane == 0) {
+    s_part[wave][0] = M;
+    s_part[wave][1] = L;
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) s_part[wave][2 + lane * DPL + e] = acc[e];
+  __syncthreads();
+  if (wave != 0) return;
+  M = fmaxf(fmaxf(s_part[0][0], s_part[1][0]), fmaxf(s_part[2][0], s_part[3][0]));
+  const float Mu = M == -INFINITY ? 0.f : M;
+  L = 0.f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float sc = __builtin_amdgcn_exp2f(s_part[w][0] - Mu);
+    L = fmaf(sc, s_part[w][1], L);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(sc, s_part[w][2 + lane * DPL + e], acc[e]);
+  }
+  if (fused) {
+    if (n > 0) {  // the newest token as one more piece: m = scale <q, k>, l = 1, o = v
+      float qf[DPL], kf[DPL], vf[DPL];
+      bits_to_float<T, DPL>(qw, qf);
+      bits_to_float<T, DPL>(kw, kf);
+      bits_to_float<T, DPL>(vw, vf);
+      float sd = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) sd = fmaf(qf[e], kf[e], sd);
+      const float ms = group_sum<64>(sd) * nt.scale_log2e;
+      const float Mn = fmaxf(M, ms);
+      const float rescale = __builtin_amdgcn_exp2f(M - Mn);
+      const float wn = __builtin_amdgcn_exp2f(ms - Mn);
+      L = fmaf(L, rescale, wn);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(acc[e], rescale, wn * vf[e]);
+    }
+    // one wavefront per kv head stores the step's K/V rows (bit for bit) into their slot
+    if (h % (Hq / Hkv) == 0 && slot >= 0 && (int64_t)slot < nt.num_slots) {
+      const int64_t off = (int64_t)slot * Hkv * D + (int64_t)g * D + lane * DPL;
+      *reinterpret_cast<Bits*>(reinterpret_cast<T*>(nt.k_cache) + off) = kw;
+      *reinterpret_cast<Bits*>(reinterpret_cast<T*>(nt.v_cache) + off) = vw;
+    }
+  }
+  if (n == 0) L = 1.f;  // a sequence with context length 0 gets a zero row
+  const float inv = 1.f / L;
+  T* dst = out + (int64_t)row * D + lane * DPL;
+  if constexpr (DPL == 2) {
+    if constexpr (Elem<T>::kBytes == 2) {
+      *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    } else {
+      *reinterpret_cast<float2*>(dst) = float2{acc[0] * inv, acc[1] * inv};
+    }
+  } else {
+    Elem<T>::store(dst, acc[0] * inv);
+  }
+}
+
+// Calls of at most this many (sequence, q head) rows merge with one workgroup per row
+// (decode_combine_wide_kernel). Measured per layer of a recorded 28-layer decode step, 16 q
+// heads: batch 1 17.7 -> 15.7 us with the wide merge (one wavefront per row before), batch 4
+// 21.8 -> 19.4, batch 16 -2 us; batch 64 (1024 rows) +0.5 us, so many rows keep one
+// wavefront per row.
 constexpr int kCombineFewRows = 256;
 
 template <typename T, int D, int G, int NI, int HPW>
@@ -618,12 +755,12 @@ static int run_decode(const DecodeArgs& a, hipStream_t stream) {
   nt.scale_log2e = c;
   const dim3 cgrid((unsigned)((rows + 3) / 4));
   if (rows <= kCombineFewRows)
-    hipLaunchKernelGGL((decode_combine_kernel<T, D, true>), cgrid, dim3(256), 0, stream,
-                       (T*)a.out, a.context_lens, (int32_t)cap, rows, a.num_heads,
+    hipLaunchKernelGGL((decode_combine_wide_kernel<T, D>), dim3((unsigned)rows), dim3(256), 0,
+                       stream, (T*)a.out, a.context_lens, (int32_t)cap, rows, a.num_heads,
                        a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, HPW > 0 ? 1 : 0,
                        nt);
   else
-    hipLaunchKernelGGL((decode_combine_kernel<T, D, false>), cgrid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((decode_combine_kernel<T, D>), cgrid, dim3(256), 0, stream,
                        (T*)a.out, a.context_lens, (int32_t)cap, rows, a.num_heads,
                        a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, HPW > 0 ? 1 : 0,
                        nt);
@@ -631,11 +768,16 @@ static int run_decode(const DecodeArgs& a, hipStream_t stream) {
 }
 
 // Whole token rows per workgroup when the kv heads split evenly over its 4 wavefronts and
-// one load instruction still covers whole rows; otherwise one head per wavefront share.
+// one load instruction still covers whole rows; otherwise one head per wavefront share. A
+// call too small to give every workgroup of the grid a full share also takes one head per
+// wavefront: its shares then start four times as many key streams at once (measured, per
+// layer of a recorded 28-layer step with 8 kv heads: batch 1 -2.0 us, batch 4 -1.9 us).
 template <typename T, int D, int G, int NI>
 static int run_decode_hpw(const DecodeArgs& a, hipStream_t s) {
   constexpr int LPR = D / Elem<T>::kPerChunk;
-  switch (a.num_kv_heads % 4 == 0 ? a.num_kv_heads / 4 : 0) {
+  const bool small = (int64_t)a.num_seqs * a.max_blocks_per_seq * a.block_size <
+                     (int64_t)a.max_workgroups * a.partition;
+  switch (a.num_kv_heads % 4 == 0 && !small ? a.num_kv_heads / 4 : 0) {
     case 1: return run_decode<T, D, G, NI, 1>(a, s);
     case 2:
       if constexpr (2 * LPR <= 64) return run_decode<T, D, G, NI, 2>(a, s);

@@ -84,7 +84,8 @@ def test_decode_partition_sizes(part):
 
 
 # One segment cut into ~141 pieces (64-key shares over a 9000-key sequence): the combine
-# merges its slots 64 at a time, so the rounds past the first 64 slots run.
+# merges its slots 64 at a time, so the rounds past the first 64 slots run; others of ~32
+# and ~65 pieces spread over two to four wavefronts of the few-rows combine.
 LONG = [
     # (dtype, D, Hq, Hkv, fused): Hkv 8 gives workgroup-owned shares of whole token rows,
     # Hkv 2 wavefront-owned shares over (sequence, kv head) segments
@@ -98,7 +99,7 @@ LONG = [
 @pytest.mark.parametrize("case", range(len(LONG)))
 def test_decode_segment_of_more_than_64_pieces(case):
     dtype, D, Hq, Hkv, fused = LONG[case]
-    w = make_decode(210 + case, [9000, 5, 300, 4160], Hq=Hq, Hkv=Hkv, D=D, dtype=dtype,
+    w = make_decode(210 + case, [9000, 5, 300, 4160, 2000], Hq=Hq, Hkv=Hkv, D=D, dtype=dtype,
                     bs=256, name=f"long{case}")
     print(f"case {case}: {dtype} D {D} Hq {Hq} Hkv {Hkv} fused {fused}", flush=True)
     ds = DeviceStep(w, partition_size=64)
@@ -111,15 +112,17 @@ def test_decode_segment_of_more_than_64_pieces(case):
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(16, 8, 128), (16, 2, 64)])
 def test_decode_few_row_combine_is_bitwise_the_general_one(Hq, Hkv, D):
-    """Calls of at most 256 (sequence, q head) rows merge their partials with a combine that
-    loads more slots up front; it must give the same bits as the general combine. The same
-    16 sequences go through both: alone (256 rows) and with a 17th, empty sequence (272
-    rows); 256-key shares and the unchanged keys keep the split identical."""
+    """Calls of at most 256 (sequence, q head) rows merge their partials with one workgroup per
+    row, its first wavefront taking slots 0 - 15; with at most 16 pieces per row that is the
+    general combine's order of operations, so it must give the same bits. The same 16
+    sequences go through both: alone (256 rows) and with a 17th, empty sequence (272 rows);
+    512-key shares (at most 9 pieces of a 4096-key row) and the unchanged keys keep the split
+    identical."""
     ctx = [3000, 1, 2048, 4095, 700, 2500, 1500, 3999, 256, 257, 3100, 2222, 900, 4000, 1234,
            2600, 5]
     w = make_decode(230 + Hkv, ctx, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16", bs=256,
                     name=f"few_rows_h{Hkv}")
-    ds = DeviceStep(w, partition_size=256)
+    ds = DeviceStep(w, partition_size=512)
     ds.store()
     ds.context_lens[16] = 0
     ds.attend()                                   # 272 rows: the general combine
@@ -128,7 +131,7 @@ def test_decode_few_row_combine_is_bitwise_the_general_one(Hq, Hkv, D):
     few = torch.full_like(general, float("nan"))
     B.paged_attn_decode(few, ds.q[:16], ds.k_cache, ds.v_cache, ds.block_tables[:16],
                         ds.context_lens[:16], w.scale, workspace=ds.workspace,
-                        partition_size=256)       # 256 rows: the few-rows combine
+                        partition_size=512)       # 256 rows: the few-rows combine
     torch.cuda.synchronize()
     assert torch.equal(general.view(torch.int16), few.view(torch.int16))
     assert bool(torch.isfinite(few.float()).all())
