@@ -78,9 +78,26 @@ class CacheFlush:
         self.buf.fill_(self.val)
 
 
-def _median_event_ms(torch, fn, iters, warmup, stream, flush=None):
+# Secondary workloads run their own calls for this long before timing: the part raises its
+# clocks only under sustained load (varlen prefill: 94.8 us after 5 back-to-back calls, 80.3
+# after 200, 78.2 after 1000, and ~94 again after half a second idle), so a few warm-up calls
+# would time a part still ramping up rather than the steady state a serving loop runs in.
+SECONDARY_WARMUP_S = 0.25
+
+
+def _median_event_ms(torch, fn, iters, warmup, stream, flush=None, warmup_s=SECONDARY_WARMUP_S):
+    """Median, p10 and p90 (ms) of `fn` bracketed by events on `stream`, each timed run
+    preceded (outside the bracket) by `flush`. Before timing: `warmup` calls, then more calls
+    until `warmup_s` seconds have passed."""
     for _ in range(warmup):
         fn()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < warmup_s:
+        fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
     torch.cuda.synchronize()
@@ -564,7 +581,9 @@ def main():
     if not args.no_secondary:
         flush = None if args.no_flush else CacheFlush(torch)
         line["secondary_timing"] = ("HIP events around each call on its stream; median of "
-                                    f"{args.iters} runs after 5 warm-ups; "
+                                    f"{args.iters} runs after 5 warm-up calls and "
+                                    f"{SECONDARY_WARMUP_S} s more of the workload's own calls "
+                                    "(steady-state clocks); "
                                     + ("no flush" if flush is None else
                                        "a 1 GiB buffer rewritten before each timed run"))
         print("bench: prefill workloads", file=sys.stderr, flush=True)
