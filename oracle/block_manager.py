@@ -33,6 +33,12 @@ manager computes, restated:
 Pins: tests/test_block_manager.py checks this against hand-derived outcomes of short
 scenarios (prefix hits, shared references, revival of a freed block, eviction, the
 growth rule at block boundaries) and the hash against the XXH64 test vector.
+
+Parity unpinned: the chained hash's byte layout (the previous hash as 8 little-endian
+bytes, then the token ids as int64 little-endian). The page prints no hash value, so
+beyond the XXH64 specification's value for the empty input nothing outside this file fixes
+the layout; it is the reading of the page's compute_hash listing (to_bytes(8, "little"),
+then a numpy int64 array's bytes). The policy is pinned; only the hash bytes are not.
 """
 from __future__ import annotations
 
