@@ -412,8 +412,10 @@ __device__ __forceinline__ void bits_to_float(const typename LaneBits<T, DPL>::t
 // the o rows of the first kSpec slots and, for the fused store, q and the newest token's
 // rows; then the o rows of the remaining slots, up to 16 at a time, D / 64 consecutive floats
 // per lane (one coalesced row per load instruction). A row cut into at most kSpec pieces
-// needs no second round.
-template <typename T, int D>
+// needs no second round. kSpec is 16 for calls of at most 128 sequences, whose rows are cut
+// into more pieces (a share then covers a few hundred keys), and 4 for larger ones, where
+// most rows have one or two pieces and 16 speculative rows per row would be mostly wasted.
+template <typename T, int D, int kSpec>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     T* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t cap,
     int32_t num_rows, int32_t Hq, int32_t Hkv, int32_t max_pieces,
@@ -421,7 +423,6 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     const int32_t* __restrict__ ws_meta, int32_t per_seq_line, NewTokens nt) {
   constexpr int DPL = D / 64;  // floats per lane
   constexpr int OB = 16;       // o rows per load batch
-  constexpr int kSpec = 4;     // o rows loaded in the first round, before the count is known
   static_assert(DPL == 1 || DPL == 2, "head_dim 64 or 128");
   typedef typename LaneBits<T, DPL>::type Bits;
   const int lane = threadIdx.x & 63;
@@ -720,6 +721,9 @@ __global__ __launch_bounds__(256) void decode_combine_wide_kernel(
 // 21.8 -> 19.4, batch 16 -2 us; batch 64 (1024 rows) +0.5 us, so many rows keep one
 // wavefront per row.
 constexpr int kCombineFewRows = 256;
+// Larger calls of at most this many sequences load the o rows of 16 slots in the combine's
+// first round (batch 64, ~9 pieces per row: 94.7 -> 94.2 us per call, four alternating runs).
+constexpr int kCombineSpec16Seqs = 128;
 
 template <typename T, int D, int G, int NI, int HPW>
 static int run_decode(const DecodeArgs& a, hipStream_t stream) {
@@ -759,8 +763,13 @@ static int run_decode(const DecodeArgs& a, hipStream_t stream) {
                        stream, (T*)a.out, a.context_lens, (int32_t)cap, rows, a.num_heads,
                        a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, HPW > 0 ? 1 : 0,
                        nt);
+  else if (a.num_seqs <= kCombineSpec16Seqs)
+    hipLaunchKernelGGL((decode_combine_kernel<T, D, 16>), cgrid, dim3(256), 0, stream,
+                       (T*)a.out, a.context_lens, (int32_t)cap, rows, a.num_heads,
+                       a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, HPW > 0 ? 1 : 0,
+                       nt);
   else
-    hipLaunchKernelGGL((decode_combine_kernel<T, D>), cgrid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((decode_combine_kernel<T, D, 4>), cgrid, dim3(256), 0, stream,
                        (T*)a.out, a.context_lens, (int32_t)cap, rows, a.num_heads,
                        a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, HPW > 0 ? 1 : 0,
                        nt);
