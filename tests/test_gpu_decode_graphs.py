@@ -218,3 +218,29 @@ def test_layered_graph_of_a_whole_model_depth():
     for l in range(28):
         assert torch.equal(_bits(eager[l][:bucket]), _bits(first[l])), f"layer {l}"
     st.graphs.close()
+
+
+def test_layered_graph_with_streaming_loads():
+    """The layered recording with a per-row kv_stream_from buffer (every K/V row streamed, as
+    the bench's 28-layer leg uses it): each layer matches its oracle and equals, bit for
+    bit, the eager layer-by-layer calls made with the same buffer."""
+    ws = _layered_workloads(2)
+    layers = [DeviceStep(w, table_width=W) for w in ws]
+    st = LayeredGraphDecodeStep(layers, 24, kv_stream_from=0)
+    refs = [run_workload(w)[0] for w in ws]
+    stream = torch.cuda.current_stream()
+    seqs = np.random.Generator(np.random.PCG64(21)).choice(ws[0].num_seqs, size=11, replace=False)
+    st.load(seqs)
+    bucket = st.graphs.bucket(11)
+    st.launch(11, stream)
+    torch.cuda.synchronize()
+    for l, ref in enumerate(refs):
+        assert_attention_close(st.out[l][:11].double().cpu().numpy(), ref[seqs],
+                               label=f"streamed layer {l}")
+    first = [o[:bucket].clone() for o in st.out]
+    eager = [torch.empty_like(o) for o in st.out]
+    st.eager(11, out=eager, stream=stream)
+    torch.cuda.synchronize()
+    for l in range(len(ws)):
+        assert torch.equal(_bits(eager[l][:bucket]), _bits(first[l])), f"layer {l}"
+    st.graphs.close()
