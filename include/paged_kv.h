@@ -352,8 +352,8 @@ int pkv_decode_graphs_destroy(pkv_decode_graphs* handle);
  * tile with one (tiles are counted back from the sequence's last row). Rows of other
  * sequences are unaffected.
  * Supported: bf16 only (fp32 accumulation); D in {64, 128}; G in {1, 2, 4, 8}; bs a power
- * of two >= 16; num_seqs <= 65535 and ceil(min(max_seqlen_k, max_blocks_per_seq * bs) / 64)
- * <= 65535. Errors: PKV_ERR_INVALID (also max_seqlen_k < max_seqlen_q),
+ * of two >= 16; Hkv * D < 2^24; num_seqs <= 65535 and
+ * ceil(min(max_seqlen_k, max_blocks_per_seq * bs) / 64) <= 65535. Errors: PKV_ERR_INVALID (also max_seqlen_k < max_seqlen_q),
  * PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.
  * -------------------------------------------------------------------------------------*/
 int paged_attn_prefill_varlen(void* out, const void* q,
@@ -386,7 +386,7 @@ int paged_attn_prefill_varlen(void* out, const void* q,
  * Lk <= max_seqlen_k (a sequence breaking this may have rows left unwritten); the rows
  * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 exist in k and v.
  * Supported: bf16 only (fp32 accumulation); D in {64, 128}; G in {1, 2, 4, 8};
- * num_seqs <= 65535; ceil(max_seqlen_k / 64) <= 65535; token strides < 2^31 / 64.
+ * num_seqs <= 65535; ceil(max_seqlen_k / 64) <= 65535; token strides < 2^24 elements.
  * Errors: PKV_ERR_INVALID (also max_seqlen_k < max_seqlen_q, bad strides or alignment),
  * PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.
  * -------------------------------------------------------------------------------------*/

@@ -430,10 +430,13 @@ int prefill_common(void* out, const void* q, const void* k, const void* v, int32
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (!supported_group(num_heads, num_kv_heads)) return PKV_ERR_UNSUPPORTED;
   if (!packed && (int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PKV_ERR_INVALID;
+  // a 64-row tile is read with 32-bit byte offsets from its first row: 64 rows of at most
+  // 2 * stride bytes each must stay below 2^31
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (row > (INT32_MAX >> 7)) return PKV_ERR_UNSUPPORTED;
   if (packed) {
-    const int64_t row = (int64_t)num_kv_heads * head_dim;
     if (k_stride < row || v_stride < row || k_stride % 8 || v_stride % 8) return PKV_ERR_INVALID;
-    if (k_stride > INT32_MAX / 64 || v_stride > INT32_MAX / 64) return PKV_ERR_UNSUPPORTED;
+    if (k_stride > (INT32_MAX >> 7) || v_stride > (INT32_MAX >> 7)) return PKV_ERR_UNSUPPORTED;
   }
   // the launch has one plane per possible count of 64-key tiles of a unit
   const int64_t key_cap = packed ? INT32_MAX : (int64_t)max_blocks_per_seq * block_size;

@@ -10,14 +10,16 @@
 // Units are dispatched longest first (most 64-key tiles) so that short units fill the slots
 // the long ones leave. Each of the 4 wavefronts owns 16 query positions x GH heads.
 //
-// Key tiles of 64 keys go from HBM straight into LDS with global_load_lds_dwordx4 (no
+// Key tiles of 64 keys go from HBM straight into LDS with 16-byte buffer_load ... lds (no
 // register staging), double-buffered: the loads of tile t+1 are issued right after the
-// barrier that publishes tile t, and the block-table entries of tile t+2 are fetched
-// behind them, so one barrier per tile is all the synchronisation there is. In LDS a K
+// barrier that publishes tile t, and the block id of tile t+2 is looked up behind them (in
+// a register window of the block table), so one barrier per tile is all the
+// synchronisation there is. In LDS a K
 // row keeps its 16-byte chunks XOR-swizzled by the row index and a V row its 32-byte
 // chunks, so the MFMA operand reads below hit distinct banks.
 //   S^T = K Q^T   v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 dims of K (one ds_read_b128
-//                 per lane), B = Q^T held in registers for the whole unit. Lane l ends with
+//                 per lane, read one k-step ahead), B = Q^T held in registers for the
+//                 whole unit. Lane l ends with
 //                 4 keys of query column l % 16, so the running max, exp2 and the running sum
 //                 stay per lane (two cross-lane steps per tile for the max).
 //   O^T += V^T P^T  same MFMA: B = the lane's own probabilities (bf16); A = V^T, read with
@@ -59,12 +61,27 @@ __device__ __forceinline__ float rows_max(float x) {
 // wait placement knows every earlier vector-memory result has landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane. The builtin
-// exists only for the device target; the host pass of this file must not see it (it would
-// drop the kernels' launch stubs), so the body is compiled for the device pass only.
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane (the
+// small-block path, whose rows lie in different blocks: a lane's offset into the pool need
+// not fit 32 bits). The builtin exists only for the device target; the host pass of this
+// file must not see it (it would drop the kernels' launch stubs), so the body is compiled
+// for the device pass only.
 __device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+#endif
+}
+
+// The same through a buffer load (MUBUF) from the wave-uniform base + voff bytes (a tile
+// inside one block, or packed rows: offsets of at most 63 rows). The global form is a
+// FLAT-encoded instruction, and while one is in flight the compiler waits for every
+// outstanding LDS read (lgkmcnt 0) wherever it needs one of them; with the buffer form it
+// waits for just the reads it needs.
+__device__ __forceinline__ void load_lds16_buf(const void* base, int voff, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, 0, 0, 0);
 #endif
 }
 
@@ -166,10 +183,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       lane_off_v[i] = lrow[i] * (int)v_stride + g * D + 8 * vchunk[i];
     }
     int nblk[NL];  // block ids of this lane's rows for a tile two steps ahead
+    // BIG_BLOCKS: lane l holds table column wbase + l (a vector load, so no scalar load is
+    // in flight in the tile loop to force full lgkmcnt waits on the LDS reads)
+    int win = -1, wbase = 0;
+    const int ncols = (Lk + bs_mask) >> bs_log2;
+    auto load_window = [&](int base) {
+      wbase = base;
+      const int c = base + lane;
+      win = c < ncols ? bt[c] : -1;
+    };
     auto fetch_blocks = [&](int kt) {
       if constexpr (PACKED) return;
-      if constexpr (BIG_BLOCKS) {  // one id, the same for every lane (nblk[1..] unused)
-        nblk[0] = kt < n_kt ? bt[(kt * kBK) >> bs_log2] : -1;
+      if constexpr (BIG_BLOCKS) {  // the tile's table column (nblk[1..] unused)
+        if (kt < n_kt) {
+          const int c = (kt * kBK) >> bs_log2;
+          if (c - wbase >= 64) load_window(c);
+          nblk[0] = c;
+        } else {
+          nblk[0] = -1;
+        }
         return;
       }
   #pragma unroll
@@ -186,7 +218,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
           base_k = (k_row0 + kt * kBK) * k_stride;
           base_v = (k_row0 + kt * kBK) * v_stride;
         } else {
-          const int b0 = __builtin_amdgcn_readfirstlane(blk[0]);
+          const int c0 = __builtin_amdgcn_readfirstlane(blk[0]);
+          const int b0 = c0 >= 0 ? __builtin_amdgcn_readlane(win, c0 - wbase) : -1;
           blk_ok = (unsigned)b0 < (unsigned)num_blocks;
           base_k = blk_ok ? ((int64_t)b0 << bs_log2 | ((kt * kBK) & bs_mask)) * row_elems : 0;
           base_v = base_k;
@@ -196,8 +229,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
         if (blk_ok && (kt + 1) * kBK <= Lk) {  // a full tile of real keys: loads only
   #pragma unroll
           for (int i = 0; i < NL; ++i) {
-            load_lds16(kb + lane_off_k[i], &dst[0][(wave * NL + i) * 1024]);
-            load_lds16(vb + lane_off_v[i], &dst[1][(wave * NL + i) * 1024]);
+            load_lds16_buf(kb, 2 * lane_off_k[i], &dst[0][(wave * NL + i) * 1024]);
+            load_lds16_buf(vb, 2 * lane_off_v[i], &dst[1][(wave * NL + i) * 1024]);
           }
           return;
         }
@@ -207,8 +240,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
           char* kdst = &dst[0][(wave * NL + i) * 1024];
           char* vdst = &dst[1][(wave * NL + i) * 1024];
           if (blk_ok && j < Lk) {
-            load_lds16(kb + lane_off_k[i], kdst);
-            load_lds16(vb + lane_off_v[i], vdst);
+            load_lds16_buf(kb, 2 * lane_off_k[i], kdst);
+            load_lds16_buf(vb, 2 * lane_off_v[i], vdst);
           } else {
             // past the sequence: zeros; a bad block id: NaN (poisons only this sequence's rows)
             const u32x4_t fill = j < Lk ? Elem<__bf16>::nan_chunk() : u32x4_t{0u, 0u, 0u, 0u};
@@ -274,6 +307,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 
     int cblk[NL];
     if (n_kt > 0) {
+      if constexpr (BIG_BLOCKS && !PACKED) load_window(0);
       fetch_blocks(0);
   #pragma unroll
       for (int i = 0; i < NL; ++i) cblk[i] = nblk[i];
@@ -299,16 +333,35 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       for (int mt = 0; mt < 4; ++mt)
   #pragma unroll
         for (int nt = 0; nt < GH; ++nt) sacc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      bf16x8_t ka[2][4];
+      auto kread = [&](int s, int mt) {
+        const int r = 16 * mt + col;
+        const int c = (4 * s + quad) ^ (r % CPR);
+        ka[s & 1][mt] = *reinterpret_cast<const bf16x8_t*>(Kt + r * ROWB + 16 * c);
+      };
   #pragma unroll
-      for (int s = 0; s < KS; ++s)
+      for (int mt = 0; mt < 4; ++mt) kread(0, mt);
+  #pragma unroll
+      for (int s = 0; s < KS; ++s) {
   #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const int r = 16 * mt + col;
-          const int c = (4 * s + quad) ^ (r % CPR);
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kt + r * ROWB + 16 * c);
+          if (s + 1 < KS) kread(s + 1, mt);
   #pragma unroll
-          for (int nt = 0; nt < GH; ++nt) sacc[mt][nt] = mfma16(a, qb[nt][s], sacc[mt][nt]);
+          for (int nt = 0; nt < GH; ++nt) sacc[mt][nt] = mfma16(ka[s & 1][mt], qb[nt][s], sacc[mt][nt]);
         }
+      }
+      // issue order: the 4 K reads of k-step 0, then each K read of step s+1 after the two
+      // MFMAs of one 16-key block of step s, then the last step's MFMAs (without it the
+      // compiler bunches the reads and waits for each pair right before its MFMAs)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  #pragma unroll
+      for (int s = 0; s + 1 < KS; ++s)
+  #pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          __builtin_amdgcn_sched_group_barrier(0x008, GH, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * GH, 0);
 
       // online softmax of the tile; the causal mask only on tiles that cross this wave's
       // diagonal. The reference max of a column (m_run) moves only when a tile's max exceeds

@@ -181,6 +181,8 @@ def test_decode_argument_validation(kw, status):
     (dict(k=ctypes.c_void_p(0x1004)), -1), (dict(v=ctypes.c_void_p(0x100c)), -1),
     # max_seqlen_k bounds every Lk >= Lq, and sizes the launch (one plane per 64-key count)
     (dict(mk=7), -1), (dict(mk=-1, mq=0), -1), (dict(W=65536, mk=1 << 23), -2),
+    # a tile's byte offsets from its first row must fit 31 bits: Hkv * D < 2^24
+    (dict(Hq=1 << 17, Hkv=1 << 17), -2),
 ])
 def test_prefill_argument_validation(kw, status):
     assert _prefill_rc(**kw) == status
@@ -225,6 +227,7 @@ def _packed_rc(**kw):
     (dict(k=ctypes.c_void_p(0x1004)), -1), (dict(v=ctypes.c_void_p(0x1008)), -1),
     (dict(out=ctypes.c_void_p(0x1002)), -1),
     (dict(mk=7), -1), (dict(mk=1 << 23), -2), (dict(B=0), 0), (dict(T=0), 0), (dict(mq=0), 0),
+    (dict(ks=1 << 24), -2), (dict(vs=1 << 24), -2),                # token strides below 2^24
 ])
 def test_packed_prefill_argument_validation(kw, status):
     assert _packed_rc(**kw) == status
