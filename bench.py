@@ -301,6 +301,34 @@ def bench_prefill_packed(torch, iters, warmup, flush=None):
             "tokens_per_s": float(w.q_lens.sum()) / (med * 1e-3)}
 
 
+def _split_report(torch, ds):
+    """The split-K layout the last decode call used, read back from its workspace: the call
+    leaves there its share size S (keys per share) followed by the prefix sums of the context
+    lengths it split. Every share covers S consecutive keys of the sequences laid end to end,
+    so a sequence is cut into as many pieces as the shares its keys touch; the histogram of
+    pieces per sequence is the partition count the combine merges."""
+    ctx = np.asarray(ds.w.seq_lens, dtype=np.int64)
+    cum = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
+    nb = ds.workspace.numel() // 4 * 4
+    words = ds.workspace[:nb].view(torch.int32).cpu().numpy()
+    n = len(cum)
+    hits = np.flatnonzero(words == cum[-1])
+    start = next((int(h) - n + 1 for h in hits
+                  if h - n + 1 >= 1 and np.array_equal(words[h - n + 1:h + 1], cum)), None)
+    if start is None:
+        return None
+    S = int(words[start - 1])
+    first = cum[:-1] // S
+    last = (cum[1:] - 1) // S
+    pieces = np.where(ctx > 0, last - first + 1, 0)
+    vals, counts = np.unique(pieces, return_counts=True)
+    total = int(cum[-1])
+    shares = -(-total // S)
+    return {"share_keys": S, "shares": shares, "keys": total,
+            "keys_per_share_mean": total / shares,
+            "pieces_per_sequence_hist": {int(v): int(c) for v, c in zip(vals, counts)}}
+
+
 def bench_large_decode(torch, iters, warmup, flush=None):
     """The 512-sequence decode workload. Half its sequences share 2-8 leading blocks (a
     common prompt prefix); the caller, which knows each table's shared leading blocks from
@@ -320,7 +348,8 @@ def bench_large_decode(torch, iters, warmup, flush=None):
             "unique_gbs": uniq / (med * 1e-3) / 1e9, "logical_gbs": logi / (med * 1e-3) / 1e9,
             "frac_hbm_unique": uniq / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "tokens_per_s": w.num_seqs / (med * 1e-3), "shared_hist": w.meta.get("shared_hist"),
-            "kv_stream_from": "per sequence: its count of shared leading blocks"}
+            "kv_stream_from": "per sequence: its count of shared leading blocks",
+            "split": _split_report(torch, ds)}
 
 
 def bench_tiny_decode(torch, iters, warmup, flush=None):
