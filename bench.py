@@ -212,24 +212,31 @@ def bench_decode_headline(torch, args):
     def timed(fn):
         for i in range(args.warmup):
             fn(i)
-        # exactly K steps between two synchronisations; each call is bracketed by events on
-        # the launch stream for the per-launch kernel time
+        # exactly K steps between two synchronisations. Calls stride, 2 stride, ... (1-based)
+        # are bracketed by events on the launch stream for the per-launch time: two event
+        # records between consecutive calls cost ~4 us of wall time per step (measured:
+        # 97.7-98.3 vs 93.4 us per step), which bracketing every call would charge to the
+        # throughput
+        stride = max(1, args.steps // max(5, args.steps // 8))
         tm = timer()
-        ev = [(tm.event(), tm.event()) for _ in range(args.steps)]
+        ev = [(tm.event(), tm.event()) for _ in range(args.steps // stride)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            tm.record(ev[i][0], stream)
+            rec = (i + 1) % stride == 0
+            if rec:
+                tm.record(ev[i // stride][0], stream)
             fn(i)
-            tm.record(ev[i][1], stream)
+            if rec:
+                tm.record(ev[i // stride][1], stream)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         call_ms = np.array([tm.elapsed_ms(a, b) for a, b in ev])
         tm.release()
-        return elapsed * 1e3 / args.steps, call_ms
+        return elapsed * 1e3 / args.steps, call_ms, stride
 
-    ms_per_step, call_ms = timed(fused)
-    sep_ms_per_step, sep_call_ms = timed(separate)
+    ms_per_step, call_ms, stride = timed(fused)
+    sep_ms_per_step, sep_call_ms, _ = timed(separate)
     step_bytes_dec, kv = decode_bytes(w)
     step_bytes = step_bytes_dec + store_bytes(w)
     call_avg = float(call_ms.mean())
@@ -245,6 +252,7 @@ def bench_decode_headline(torch, args):
         "decode_call_us_avg": call_avg * 1e3,
         "decode_call_us_p10_p90": [float(np.percentile(call_ms, 10)) * 1e3,
                                    float(np.percentile(call_ms, 90)) * 1e3],
+        "decode_calls_timed": f"calls {stride}, {2 * stride}, ... of the {args.steps} timed calls, {len(call_ms)} in all",
         "separate_calls": {"ms_per_step": sep_ms_per_step,
                            "value": step_bytes / (sep_ms_per_step * 1e-3) / 1e9,
                            "call_us_avg": float(sep_call_ms.mean()) * 1e3},
@@ -679,6 +687,7 @@ def main():
         "tokens_per_s": head["tokens_per_s"],
         "decode_call_us_avg": head["decode_call_us_avg"],
         "decode_call_us_p10_p90": head["decode_call_us_p10_p90"],
+        "decode_calls_timed": head["decode_calls_timed"],
         "separate_calls": head["separate_calls"],
         "step_bytes": head["step_bytes"],
         "kv_bytes": head["kv_bytes"],
