@@ -157,6 +157,25 @@ def test_prefill_invalid_block_id_poisons_only_rows_that_reach_it():
     assert_attention_close(out[keep], ref[keep], rel_l2=1e-2, label="unaffected rows")
 
 
+def test_prefill_invalid_block_id_past_the_first_table_window():
+    # blocks of 64 keys: a 4500-key sequence has 71 table columns, more than the 64 a tile
+    # lookup holds at once, so the lookup reloads past column 63. Column 66 (keys 4224..4287)
+    # is bad: rows from 4224 on reach it; the 64-row query tile holding row 4224 (rows
+    # 4180..4243, tiles counted back from the last row) may be poisoned too; earlier rows
+    # and the other sequence must match the oracle.
+    w = make_prefill(315, [4500, 90], cached=[0, 70], Hq=16, Hkv=8, D=128, bs=64)
+    ds = DeviceStep(w)
+    ds.store()
+    ds.block_tables[0, 66] = w.num_blocks + 5
+    ds.attend()
+    torch.cuda.synchronize()
+    out = ds.out_f64()
+    ref, _, _, _ = run_workload(w)
+    assert np.all(np.isnan(out[4224:4500]))
+    keep = np.r_[0:4180, 4500:4590]
+    assert_attention_close(out[keep], ref[keep], rel_l2=1e-2, label="rows that do not reach it")
+
+
 def test_prefill_loose_max_seqlen_k_is_bitwise_identical():
     # a larger max_seqlen_k only adds planes of empty workgroups to the launch
     w = make_prefill(313, [333, 0, 64, 17, 900], cached=[40, 5, 0, 300, 100], Hq=16, Hkv=8,
