@@ -432,7 +432,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   const int g = h / (Hq / Hkv);
   const int64_t base = (int64_t)row * max_pieces;
   const bool fused = nt.key != nullptr;
-  // round 1
+  // first batch of loads
   const int n_raw = context_lens[b];
   const int S = ws_meta[0];
   const int cum = ws_meta[1 + b];
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[e] *= rescale;
       M = Mn;
-      // round 2: the o rows not loaded yet
+      // further batches: the o rows not loaded yet
       for (int p = 0; p < cnt; p += OB) {
         float ov[OB][DPL];
 #pragma unroll
@@ -586,7 +586,8 @@ __global__ __launch_bounds__(256) void decode_combine_wide_kernel(
   const int g = h / (Hq / Hkv);
   const int64_t base = (int64_t)row * max_pieces;
   const bool fused = nt.key != nullptr;
-  // round 1: metadata, this wavefront's first 16 slots, and (wavefront 0) the newest token
+  // first batch of loads: metadata, this wavefront's first 16 slots, and (wavefront 0) the
+  // newest token
   const int n_raw = context_lens[b];
   const int S = ws_meta[0];
   const int cum = ws_meta[1 + b];
