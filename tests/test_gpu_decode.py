@@ -226,3 +226,28 @@ def test_decode_workspace_too_small_is_rejected():
     with pytest.raises(B.PagedKVError):
         B.paged_attn_decode(ds.out, ds.q, ds.k_cache, ds.v_cache, ds.block_tables,
                             ds.context_lens, w.scale, workspace=ds.workspace[:8])
+
+
+def test_decode_split_report_reads_the_calls_layout():
+    # The bench reports the split-K layout a call used from what the call leaves in its
+    # workspace: the share size, then the prefix sums of the context lengths it split. On the
+    # batch-512 workload those must be the workload's own prefix sums, the shares must cover
+    # every key, and the pieces per sequence must add up to the (sequence, share) overlaps.
+    import bench
+    w = make_config(5)
+    ds = DeviceStep(w, kv_stream_from="shared")
+    ds.store()
+    ds.attend()
+    torch.cuda.synchronize()
+    rep = bench._split_report(torch, ds)
+    assert rep is not None, "the call's split descriptor was not found in its workspace"
+    keys = int(np.asarray(w.seq_lens, dtype=np.int64).sum())
+    S, shares = rep["share_keys"], rep["shares"]
+    assert rep["keys"] == keys
+    assert S >= 256 and (shares - 1) * S < keys <= shares * S
+    hist = {int(k): v for k, v in rep["pieces_per_sequence_hist"].items()}
+    assert sum(hist.values()) == w.num_seqs and min(hist) >= 1
+    # each share boundary inside a sequence adds one piece to it
+    cum = np.concatenate([[0], np.cumsum(np.asarray(w.seq_lens, dtype=np.int64))])
+    inner = sum(1 for k in range(1, shares) if k * S not in set(cum.tolist()))
+    assert sum(p * n for p, n in hist.items()) == w.num_seqs + inner
