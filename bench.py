@@ -349,15 +349,26 @@ def bench_large_decode(torch, iters, warmup, flush=None):
     ds.store(stream)
     med, p10, p90 = _median_event_ms(torch, lambda: ds.attend(stream), iters, warmup, stream,
                                      flush)
+    split = _split_report(torch, ds)
     uniq, kv_u = decode_bytes(w, unique=True)
     logi, kv_l = decode_bytes(w, unique=False)
+    # the same step through paged_attn_decode_prefix: each shared leading block read once for
+    # all the sequences sharing it (groups from the tables and the shared-block counts)
+    ds.prefix_setup()
+    pmed, pp10, pp90 = _median_event_ms(torch, lambda: ds.attend_prefix(stream), iters, warmup,
+                                        stream, flush)
+    prefix = {"call": "paged_attn_decode_prefix", "decode_us_median": pmed * 1e3,
+              "decode_us_p10_p90": [pp10 * 1e3, pp90 * 1e3],
+              "unique_gbs": uniq / (pmed * 1e-3) / 1e9,
+              "frac_hbm_unique": uniq / (pmed * 1e-3) / 1e9 / HBM_PEAK_GBS,
+              "groups": ds.pfx["num_groups"], "largest_group": ds.pfx["max_group_size"]}
     return {"workload": CONFIG_NAMES[5], "decode_us_median": med * 1e3,
             "decode_us_p10_p90": [p10 * 1e3, p90 * 1e3],
             "unique_gbs": uniq / (med * 1e-3) / 1e9, "logical_gbs": logi / (med * 1e-3) / 1e9,
             "frac_hbm_unique": uniq / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "tokens_per_s": w.num_seqs / (med * 1e-3), "shared_hist": w.meta.get("shared_hist"),
             "kv_stream_from": "per sequence: its count of shared leading blocks",
-            "split": _split_report(torch, ds)}
+            "split": split, "prefix_call": prefix}
 
 
 def bench_tiny_decode(torch, iters, warmup, flush=None):

@@ -219,6 +219,48 @@ int paged_attn_decode_noalloc(void* out, const void* q,
                               hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * Decode attention with shared prefix blocks read once - [P1] Attention.forward, decode
+ * branch, for a batch whose block tables share leading blocks ([P1] BlockManager.allocate:
+ * a cached block is reused by every sequence whose token prefix hashes to it, so only
+ * leading full blocks are shared, each in the same table column of all its sharers).
+ * Same operation and arguments as paged_attn_decode (attention only), except that:
+ *   shared_cols  device int32 [num_seqs]: sequence b's count of shared leading columns
+ *                (0 = none); its keys from shared_cols[b] * bs on go through the split-K
+ *                stream (read with non-temporal loads), the keys before through the groups.
+ *   group_ptr, group_members, group_col  device int32 arrays describing the groups: group
+ *                g is sequences group_members[group_ptr[g] .. group_ptr[g+1]-1], all holding
+ *                one block in table column group_col[g]; [num_groups + 1], [group_ptr[
+ *                num_groups]] and [num_groups] entries. Each group's block is read once per
+ *                64 members and its keys multiplied out with bf16 MFMA for all of them.
+ *   num_groups, max_group_size  host ints: the group count and an upper bound of every
+ *                group's member count (it sizes the launch).
+ *   workspace    at least paged_attn_decode_prefix_workspace_bytes(...) bytes (the decode
+ *                call's slots plus (D + 2) floats per (sequence, q head, table column)).
+ * Preconditions: for every b and c < shared_cols[b], exactly one group with column c holds
+ * b, and every member of a group holds the same block id in that column; shared_cols[b] *
+ * bs <= context_lens[b] - 1 (the newest token's block is private). A column left without a
+ * group is merged from whatever its slot holds.
+ * Supported: bf16 only; block_size >= 64; Hkv * D < 2^24; num_groups <= 65535; the decode
+ * call's other limits. Results equal paged_attn_decode's within rounding: the shared keys'
+ * probabilities are rounded to bf16 for the MFMA, as in prefill. Errors as
+ * paged_attn_decode.
+ * -------------------------------------------------------------------------------------*/
+size_t paged_attn_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                                int32_t head_dim, int32_t max_blocks_per_seq,
+                                                int32_t block_size, int32_t partition_size);
+int paged_attn_decode_prefix(void* out, const void* q,
+                             const void* k_cache, const void* v_cache, int32_t num_blocks,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs,
+                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, float scale, pkv_dtype_t dtype,
+                             int32_t partition_size, const int32_t* shared_cols,
+                             const int32_t* group_ptr, const int32_t* group_members,
+                             const int32_t* group_col, int32_t num_groups,
+                             int32_t max_group_size, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * Decode attention with the step's store fused in - [P1] Attention.forward, decode branch:
  * store_kvcache of the step's K/V rows, then the decode attention over the cache.
  * Same result as store_kvcache(key, value, k_cache, v_cache, slot_mapping[0 .. num_seqs))

@@ -14,6 +14,9 @@ from ._binding import (  # noqa: F401
     load_library,
     paged_attn_decode,
     paged_attn_decode_noalloc,
+    paged_attn_decode_prefix,
+    paged_attn_decode_prefix_workspace_bytes,
+    prefix_groups,
     paged_attn_decode_store,
     paged_attn_decode_workspace_bytes,
     paged_attn_prefill_varlen,
@@ -32,7 +35,8 @@ from ._binding import (  # noqa: F401
 
 __all__ = [
     "PKV_BF16", "PKV_F32", "BlockManager", "DecodeGraphs", "PagedKVError", "attn_prefill_varlen",
-    "load_library", "paged_attn_decode", "paged_attn_decode_noalloc", "paged_attn_decode_store",
+    "load_library", "paged_attn_decode", "paged_attn_decode_noalloc", "paged_attn_decode_prefix",
+    "paged_attn_decode_prefix_workspace_bytes", "prefix_groups", "paged_attn_decode_store",
     "paged_attn_decode_workspace_bytes", "paged_attn_prefill_varlen", "pkv_decode_metadata",
     "pkv_block_hash", "pkv_prefill_metadata", "pkv_sample", "pkv_sample_workspace_bytes",
     "pkv_status_string", "pkv_xxh64", "store_kvcache", "PreconditionError", "pkv_check_decode",

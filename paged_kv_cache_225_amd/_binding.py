@@ -37,6 +37,10 @@ SIGNATURES = {
                                    _i32, _f, _c_int, _i32, _p, _p, _size, _p]),
     "paged_attn_decode_noalloc": (_c_int, [_p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32,
                                            _i32, _i32, _f, _c_int, _i32, _p, _p]),
+    "paged_attn_decode_prefix_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "paged_attn_decode_prefix": (_c_int, [_p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32,
+                                          _i32, _i32, _f, _c_int, _i32, _p, _p, _p, _p, _i32,
+                                          _i32, _p, _size, _p]),
     "paged_attn_decode_store": (_c_int, [_p, _p, _p, _i64, _p, _i64, _p, _p, _p, _i32, _p, _i32,
                                          _p, _i32, _i32, _i32, _i32, _i32, _f, _c_int, _i32, _p,
                                          _p, _size, _p]),
@@ -267,6 +271,55 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
         _dtype_code(q), partition_size, _t_ptr(kv_stream_from), _t_ptr(workspace), ws_bytes,
         _stream(stream))
     _check("paged_attn_decode", rc)
+
+
+def paged_attn_decode_prefix_workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                                             block_size, partition_size=0):
+    return int(load_library().paged_attn_decode_prefix_workspace_bytes(
+        num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size, partition_size))
+
+
+def paged_attn_decode_prefix(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                             shared_cols, group_ptr, group_members, group_col, max_group_size,
+                             workspace=None, partition_size=0, stream=None):
+    """paged_attn_decode with each shared leading block read once for all its sharers:
+    shared_cols int32 [B] per sequence; group_ptr / group_members / group_col int32 device
+    tensors (CSR: group g = members[ptr[g]:ptr[g+1]], all holding one block in column
+    col[g]); max_group_size a host int (see prefix_groups)."""
+    B, Hq, D = q.shape
+    num_blocks, bs, Hkv, _ = k_cache.shape
+    W = block_tables.shape[1]
+    G = group_col.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().paged_attn_decode_prefix(
+        _t_ptr(out), _t_ptr(q), _t_ptr(k_cache), _t_ptr(v_cache), num_blocks,
+        _t_ptr(block_tables), W, _t_ptr(context_lens), B, Hq, Hkv, D, bs, float(scale),
+        _dtype_code(q), partition_size, _t_ptr(shared_cols), _t_ptr(group_ptr),
+        _t_ptr(group_members), _t_ptr(group_col), G, int(max_group_size), _t_ptr(workspace),
+        ws_bytes, _stream(stream))
+    _check("paged_attn_decode_prefix", rc)
+
+
+def prefix_groups(block_tables, shared_cols):
+    """Host: the groups paged_attn_decode_prefix takes, from the batch's block tables (int
+    [B, W]) and each sequence's count of shared leading columns: one group per (column,
+    block id) among the shared columns, its members in sequence order. Returns numpy int32
+    (group_ptr, group_members, group_col) and the largest group's size."""
+    bt = np.asarray(block_tables)
+    sc = np.asarray(shared_cols, dtype=np.int64)
+    groups = {}
+    for b in range(bt.shape[0]):
+        for c in range(int(sc[b])):
+            groups.setdefault((c, int(bt[b, c])), []).append(b)
+    keys = sorted(groups)
+    ptr = np.zeros(len(keys) + 1, dtype=np.int32)
+    members = []
+    for i, k in enumerate(keys):
+        members += groups[k]
+        ptr[i + 1] = len(members)
+    cols = np.asarray([k[0] for k in keys], dtype=np.int32)
+    largest = max((len(v) for v in groups.values()), default=0)
+    return ptr, np.asarray(members, dtype=np.int32), cols, largest
 
 
 PKV_DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20

@@ -269,7 +269,23 @@ size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, in
 
 namespace {
 
-// The shared body of paged_attn_decode and paged_attn_decode_store (fused: the latter).
+// The shared leading blocks of a paged_attn_decode_prefix call (see the header).
+struct SharedPrefix {
+  const int32_t* cols;
+  const int32_t* group_ptr;
+  const int32_t* group_members;
+  const int32_t* group_col;
+  int32_t num_groups, max_group_size;
+};
+
+// Bytes of the shared blocks' partial slots: (D + 2) floats per (sequence, head, column).
+size_t prefix_slot_bytes(int64_t num_seqs, int64_t num_heads, int64_t head_dim, int64_t width) {
+  return (size_t)num_seqs * num_heads * width * (head_dim + 2) * sizeof(float);
+}
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// The shared body of paged_attn_decode, paged_attn_decode_store (fused) and
+// paged_attn_decode_prefix (sp: the shared leading blocks).
 int decode_common(void* out, const void* q, const void* k_cache, const void* v_cache,
                   int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
                   const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
@@ -277,8 +293,17 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
                   pkv_dtype_t dtype, int32_t partition_size, const int32_t* kv_stream_from,
                   void* workspace, size_t workspace_bytes, bool fused, const void* key,
                   int64_t key_token_stride, const void* value, int64_t value_token_stride,
-                  const int32_t* slot_mapping, bool debug_checks, hipStream_t stream) {
+                  const int32_t* slot_mapping, bool debug_checks, hipStream_t stream,
+                  const SharedPrefix* sp = nullptr) {
   if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (sp) {
+    // the shared blocks go through bf16 MFMA tiles of 64 keys, addressed with 32-bit byte
+    // offsets from a tile's first row
+    if (dtype != PKV_BF16 || block_size < 64) return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)num_kv_heads * head_dim > (INT32_MAX >> 7)) return PKV_ERR_UNSUPPORTED;
+    if (sp->num_groups < 0 || sp->max_group_size < 0) return PKV_ERR_INVALID;
+    if (sp->num_groups > 65535 || (sp->max_group_size + 63) / 64 > 65535) return PKV_ERR_UNSUPPORTED;
+  }
   if (num_seqs < 0 || num_blocks < 1 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID;
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return PKV_ERR_INVALID;
   if (!pow2_at_least_16(block_size)) return PKV_ERR_UNSUPPORTED;
@@ -301,10 +326,16 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_INVALID;
   if (fused && (!key || !value || !slot_mapping)) return PKV_ERR_INVALID;
+  if (sp && (!sp->cols || (sp->num_groups > 0 && sp->max_group_size > 0 &&
+                           (!sp->group_ptr || !sp->group_members || !sp->group_col))))
+    return PKV_ERR_INVALID;
   const size_t need = paged_attn_decode_workspace_bytes(num_seqs, num_heads, head_dim,
                                                         max_blocks_per_seq, block_size,
                                                         partition_size);
-  if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  const size_t need_all = sp ? align256(need) + prefix_slot_bytes(num_seqs, num_heads, head_dim,
+                                                                  max_blocks_per_seq)
+                             : need;
+  if (!workspace || workspace_bytes < need_all) return PKV_ERR_WORKSPACE;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
       !aligned16(workspace))
     return PKV_ERR_INVALID;
@@ -344,6 +375,30 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
   a.new_v_stride = value_token_stride;
   a.slot_mapping = slot_mapping;
   a.num_slots = (int64_t)num_blocks * block_size;
+  a.prefix = sp ? 1 : 0;
+  a.pfx = pkv::PrefixArgs{};
+  if (sp) {
+    a.kv_stream_from = sp->cols;  // the stream kernel skips (and the combine merges) them
+    pkv::PrefixArgs& p = a.pfx;
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.num_blocks = num_blocks;
+    p.block_tables = block_tables;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.group_ptr = sp->group_ptr;
+    p.group_members = sp->group_members;
+    p.group_col = sp->group_col;
+    p.num_groups = sp->num_groups;
+    p.max_group_size = sp->max_group_size;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.head_dim = head_dim;
+    p.block_size = block_size;
+    p.scale = scale;
+    p.pfx_o = (float*)((char*)workspace + align256(need));
+    p.pfx_ml = p.pfx_o + (size_t)num_seqs * num_heads * max_blocks_per_seq * head_dim;
+  }
   const int rc = pkv::launch_decode(a, stream);
   return rc == 0 ? PKV_OK : (rc == -2 ? PKV_ERR_UNSUPPORTED : PKV_ERR_HIP);
 }
@@ -364,6 +419,34 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
                        scale, dtype, partition_size, kv_stream_from, workspace, workspace_bytes,
                        false, nullptr,
                        0, nullptr, 0, nullptr, true, stream);
+}
+
+size_t paged_attn_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                                int32_t head_dim, int32_t max_blocks_per_seq,
+                                                int32_t block_size, int32_t partition_size) {
+  const size_t base = paged_attn_decode_workspace_bytes(num_seqs, num_heads, head_dim,
+                                                        max_blocks_per_seq, block_size,
+                                                        partition_size);
+  if (base == 0) return 0;
+  return align256(base) + prefix_slot_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq);
+}
+
+int paged_attn_decode_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             int32_t num_blocks, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, float scale,
+                             pkv_dtype_t dtype, int32_t partition_size,
+                             const int32_t* shared_cols, const int32_t* group_ptr,
+                             const int32_t* group_members, const int32_t* group_col,
+                             int32_t num_groups, int32_t max_group_size, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  const SharedPrefix sp{shared_cols, group_ptr, group_members, group_col, num_groups,
+                        max_group_size};
+  return decode_common(out, q, k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       scale, dtype, partition_size, nullptr, workspace, workspace_bytes, false,
+                       nullptr, 0, nullptr, 0, nullptr, true, stream, &sp);
 }
 
 int paged_attn_decode_store(void* out, const void* q, const void* key, int64_t key_token_stride,

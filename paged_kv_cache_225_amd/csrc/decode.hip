@@ -65,7 +65,11 @@ struct Chunk {
   bool piece_start, piece_end;
 };
 
-template <typename T, int D, int G, int NI, int HPW, bool NT>
+// PFX: kv_stream_from[b] is the count of sequence b's leading table columns shared with
+// other sequences of the call, whose keys another kernel takes (decode_prefix_kernel): the
+// line holds only the keys past them, all read non-temporally, and every segment leaves
+// partials for the combine.
+template <typename T, int D, int G, int NI, int HPW, bool NT, bool PFX = false>
 __global__ __launch_bounds__(256) void decode_stream_kernel(
     T* __restrict__ out, const T* __restrict__ q, const T* __restrict__ k_cache,
     const T* __restrict__ v_cache, int32_t num_blocks, const int32_t* __restrict__ block_tables,
@@ -95,6 +99,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
       const int b = base + threadIdx.x;
       int v = b < num_seqs ? clamp_ctx(context_lens[b], cap) : 0;
       v -= skip_last & (v > 0);  // the newest token comes from the step's rows
+      if constexpr (PFX) {
+        if (b < num_seqs) v = max(0, v - (kv_stream_from[b] << bs_log2));
+      }
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const int t = __shfl_up(v, off);
@@ -164,8 +171,16 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   // sequence changes or a chunk runs past it.
   int bt_b = -1, bt_base = 0, bt_reg = -1;
   int stream_from = INT32_MAX;  // first table column of sequence bt_b read non-temporally
+  int pfx_b = -1, pfx_keys = 0;  // PFX: the shared leading keys of sequence pfx_b
   auto issue = [&](const Chunk& c, u32x4_t* kr, u32x4_t* vr) {
-    const int first = c.k >> bs_log2, last = (c.k + c.cnt - 1) >> bs_log2;
+    if constexpr (PFX) {
+      if (c.b != pfx_b) {
+        pfx_b = c.b;
+        pfx_keys = kv_stream_from[c.b] << bs_log2;
+      }
+    }
+    const int k0 = PFX ? c.k + pfx_keys : c.k;  // the chunk's first key in the sequence
+    const int first = k0 >> bs_log2, last = (k0 + c.cnt - 1) >> bs_log2;
     if (c.b != bt_b || first < bt_base || last >= bt_base + 64) {
       if constexpr (NT) {
         if (c.b != bt_b) stream_from = kv_stream_from[c.b];
@@ -184,7 +199,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int r = i * RPI + rsub;
-        const int j = c.k + r;
+        const int j = k0 + r;
         const int blk = one_block ? blk0 : __shfl(bt_reg, min((j >> bs_log2) - bt_base, 63));
         kr[i] = u32x4_t{0u, 0u, 0u, 0u};
         vr[i] = u32x4_t{0u, 0u, 0u, 0u};
@@ -306,7 +321,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
       l[h] = lt;
     }
     if (rsub == 0) {
-      const bool whole = !skip_last && piece_x0 == c.seg_start && c.x + c.cnt == c.seg_start + c.n;
+      const bool whole = !PFX && !skip_last && piece_x0 == c.seg_start &&
+                         c.x + c.cnt == c.seg_start + c.n;
       if (whole) {
         T* dst0 = out + ((int64_t)c.b * Hq + c.g * G) * D + sub * EPL;
 #pragma unroll
@@ -415,12 +431,15 @@ __device__ __forceinline__ void bits_to_float(const typename LaneBits<T, DPL>::t
 // needs no second round. kSpec is 16 for calls of at most 128 sequences, whose rows are cut
 // into more pieces (a share then covers a few hundred keys), and 4 for larger ones, where
 // most rows have one or two pieces and 16 speculative rows per row would be mostly wasted.
-template <typename T, int D, int kSpec>
+// PFX: besides the stream kernel's pieces, row (b, h) merges one piece per shared leading
+// table column of sequence b (pp.cols[b] of them), left by decode_prefix_kernel.
+template <typename T, int D, int kSpec, bool PFX = false>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     T* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t cap,
     int32_t num_rows, int32_t Hq, int32_t Hkv, int32_t max_pieces,
     const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
-    const int32_t* __restrict__ ws_meta, int32_t per_seq_line, NewTokens nt) {
+    const int32_t* __restrict__ ws_meta, int32_t per_seq_line, NewTokens nt,
+    PrefixParts pp) {
   constexpr int DPL = D / 64;  // floats per lane
   constexpr int OB = 16;       // o rows per load batch
   static_assert(DPL == 1 || DPL == 2, "head_dim 64 or 128");
@@ -463,7 +482,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     slot = nt.slot_mapping[b];
   }
   const int n = clamp_ctx(n_raw, cap);
-  const int nc = fused ? n - (n > 0) : n;  // keys the stream kernel took from the cache
+  int nc = fused ? n - (n > 0) : n;  // keys the stream kernel took from the cache
+  int pc = 0;                        // PFX: shared leading columns, merged from pp
+  if constexpr (PFX) {
+    pc = pp.cols[b];
+    nc = max(0, nc - (pc << pp.bs_log2));
+  }
   T* dst = out + (int64_t)row * D + lane * DPL;
   float acc[DPL];
 #pragma unroll
@@ -474,7 +498,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     // start of the segment on the split line: one per (sequence, kv head), or one per sequence
     const int seg_start = per_seq_line ? cum : Hkv * cum + g * nc;
     const int np = (seg_start + nc - 1) / S - seg_start / S + 1;
-    if (np == 1 && !fused) return;  // written by the stream kernel
+    if (np == 1 && !fused && !PFX) return;  // written by the stream kernel
     for (int p0 = 0; p0 < np; p0 += 64) {
       const int cnt = min(64, np - p0);
       if (p0 > 0) {  // slots past the first 64 (segments cut into more than 64 pieces)
@@ -519,6 +543,42 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
         for (int u = 0; u < OB; ++u) {
           if (p + u >= cnt) break;
           const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wp), p + u));
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, ov[u][e], acc[e]);
+        }
+      }
+    }
+  }
+  if constexpr (PFX) {
+    // the shared blocks' pieces: slot (row, column c) for c < pc
+    const int64_t pbase = (int64_t)row * pp.stride;
+    for (int p0 = 0; p0 < pc; p0 += 64) {
+      const int cnt = min(64, pc - p0);
+      float mq = -INFINITY, lq = 0.f;
+      if (lane < cnt) {
+        mq = pp.ml[2 * (pbase + p0 + lane)];
+        lq = pp.ml[2 * (pbase + p0 + lane) + 1];
+      }
+      const float Mn = fmaxf(M, group_max<64>(mq));
+      const float rescale = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+      const float wq = lane < cnt ? __builtin_amdgcn_exp2f(mq - Mn) : 0.f;
+      L = fmaf(L, rescale, group_sum<64>(wq * lq));
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] *= rescale;
+      M = Mn;
+      for (int p = 0; p < cnt; p += 8) {
+        float ov[8][DPL];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (p + u >= cnt) break;
+          const float* src = pp.o + (pbase + p0 + p + u) * D + lane * DPL;
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) ov[u][e] = src[e];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (p + u >= cnt) break;
+          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), p + u));
 #pragma unroll
           for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, ov[u][e], acc[e]);
         }
@@ -740,12 +800,25 @@ static int run_decode(const DecodeArgs& a, hipStream_t stream) {
   const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
   auto* stream_kernel = a.kv_stream_from ? decode_stream_kernel<T, D, G, NI, HPW, true>
                                          : decode_stream_kernel<T, D, G, NI, HPW, false>;
+  constexpr bool kPrefixMode = Elem<T>::kBytes == 2;  // the shared-block pass is bf16 MFMA
+  if constexpr (kPrefixMode) {
+    if (a.prefix) stream_kernel = decode_stream_kernel<T, D, G, NI, HPW, true, true>;
+  }
   hipLaunchKernelGGL(stream_kernel, dim3((unsigned)blocks), dim3(256),
                      lds, stream, (T*)a.out, (const T*)a.q, (const T*)a.k_cache,
                      (const T*)a.v_cache, a.num_blocks, a.block_tables, a.max_blocks_per_seq,
                      a.context_lens, a.num_seqs, a.num_kv_heads, bs_log2, c, a.partition,
                      a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, a.new_k != nullptr ? 1 : 0,
                      a.kv_stream_from);
+  PrefixParts pp{};
+  if constexpr (kPrefixMode) {
+    if (a.prefix) {
+      if (hipGetLastError() != hipSuccess) return -4;
+      const int rc = launch_decode_prefix(a.pfx, stream);
+      if (rc != 0) return rc;
+      pp = PrefixParts{a.kv_stream_from, a.pfx.pfx_o, a.pfx.pfx_ml, a.max_blocks_per_seq, bs_log2};
+    }
+  }
   const int rows = a.num_seqs * a.num_heads;
   NewTokens nt;
   nt.q = a.q;
@@ -759,6 +832,21 @@ static int run_decode(const DecodeArgs& a, hipStream_t stream) {
   nt.num_slots = a.num_slots;
   nt.scale_log2e = c;
   const dim3 cgrid((unsigned)((rows + 3) / 4));
+  if constexpr (kPrefixMode) {
+    if (a.prefix) {  // the shared blocks' pieces merge in the one-wavefront-per-row form
+      if (a.num_seqs <= kCombineSpec16Seqs)
+        hipLaunchKernelGGL((decode_combine_kernel<T, D, 16, true>), cgrid, dim3(256), 0, stream,
+                           (T*)a.out, a.context_lens, (int32_t)cap, rows, a.num_heads,
+                           a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta,
+                           HPW > 0 ? 1 : 0, nt, pp);
+      else
+        hipLaunchKernelGGL((decode_combine_kernel<T, D, 4, true>), cgrid, dim3(256), 0, stream,
+                           (T*)a.out, a.context_lens, (int32_t)cap, rows, a.num_heads,
+                           a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta,
+                           HPW > 0 ? 1 : 0, nt, pp);
+      return hipGetLastError() == hipSuccess ? 0 : -4;
+    }
+  }
   if (rows <= kCombineFewRows)
     hipLaunchKernelGGL((decode_combine_wide_kernel<T, D>), dim3((unsigned)rows), dim3(256), 0,
                        stream, (T*)a.out, a.context_lens, (int32_t)cap, rows, a.num_heads,
@@ -768,12 +856,12 @@ static int run_decode(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_combine_kernel<T, D, 16>), cgrid, dim3(256), 0, stream,
                        (T*)a.out, a.context_lens, (int32_t)cap, rows, a.num_heads,
                        a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, HPW > 0 ? 1 : 0,
-                       nt);
+                       nt, pp);
   else
     hipLaunchKernelGGL((decode_combine_kernel<T, D, 4>), cgrid, dim3(256), 0, stream,
                        (T*)a.out, a.context_lens, (int32_t)cap, rows, a.num_heads,
                        a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, HPW > 0 ? 1 : 0,
-                       nt);
+                       nt, pp);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

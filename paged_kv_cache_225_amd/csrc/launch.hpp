@@ -15,6 +15,35 @@ int launch_store_kvcache(const void* key, int64_t key_stride, const void* value,
                          const int32_t* slot_mapping, int32_t num_tokens, int32_t row_elems,
                          int32_t elem_bytes, hipStream_t stream);
 
+// Decode partials of shared prefix blocks: group g is the sequences group_members[group_ptr[g]
+// .. group_ptr[g+1]-1], each holding the same block in table column group_col[g].
+struct PrefixArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  int32_t num_blocks;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* group_ptr;
+  const int32_t* group_members;
+  const int32_t* group_col;
+  int32_t num_groups, max_group_size;
+  int32_t num_heads, num_kv_heads, head_dim, block_size;
+  float scale;
+  float* pfx_o;   // [num_seqs, Hq, max_blocks_per_seq, D]: slot (b, h, column)
+  float* pfx_ml;  // [num_seqs, Hq, max_blocks_per_seq, 2]
+};
+int launch_decode_prefix(const PrefixArgs& a, hipStream_t stream);
+
+// What the combine kernel reads of the shared blocks' pieces (cols == nullptr: none).
+struct PrefixParts {
+  const int32_t* cols;  // [num_seqs]: shared leading table columns of each sequence
+  const float* o;       // PrefixArgs::pfx_o
+  const float* ml;      // PrefixArgs::pfx_ml
+  int32_t stride;       // slots per (sequence, head): max_blocks_per_seq
+  int32_t bs_log2;
+};
+
 struct DecodeArgs {
   void* out;
   const void* q;
@@ -42,6 +71,10 @@ struct DecodeArgs {
   int64_t new_v_stride;
   const int32_t* slot_mapping;
   int64_t num_slots;
+  // prefix mode: kv_stream_from[b] is sequence b's count of shared leading table columns,
+  // whose keys decode_prefix_kernel takes (pfx); the stream kernel takes the rest
+  int32_t prefix;
+  PrefixArgs pfx;
 };
 
 // What the combine kernel needs for the fused store (key == nullptr: not fused).
@@ -77,5 +110,6 @@ struct PrefillArgs {
   float scale;
 };
 int launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
 
 }  // namespace pkv

@@ -147,6 +147,34 @@ class DeviceStep:
                                         self.block_tables, self.cu_seqlens_q, self.cu_seqlens_k,
                                         self.max_seqlen_q, self.max_seqlen_k, w.scale, stream=stream)
 
+    def prefix_setup(self, shared_cols=None):
+        """Decode only: the shared-prefix groups of the step's tables for
+        paged_attn_decode_prefix (shared_cols: each sequence's count of shared leading
+        columns; default the workload's shared blocks) and a workspace for it."""
+        w = self.w
+        sc = np.asarray(w.shared_blocks if shared_cols is None else shared_cols, dtype=np.int32)
+        ptr, mem, col, largest = B.prefix_groups(self.block_tables.cpu().numpy(), sc)
+        self.pfx = {"shared_cols": _i32(sc, self.device), "group_ptr": _i32(ptr, self.device),
+                    "group_members": _i32(mem if len(mem) else np.zeros(1, np.int32), self.device),
+                    "group_col": _i32(col, self.device), "max_group_size": largest,
+                    "num_groups": len(col)}
+        nbytes = B.paged_attn_decode_prefix_workspace_bytes(
+            w.num_seqs, w.num_heads, w.head_dim, self.block_tables.shape[1], w.block_size,
+            self.partition_size)
+        self.pfx_workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+        return self.pfx
+
+    def attend_prefix(self, stream=None):
+        """The step's decode attention through paged_attn_decode_prefix (prefix_setup first)."""
+        p = self.pfx
+        B.paged_attn_decode_prefix(self.out, self.q, self.k_cache, self.v_cache,
+                                   self.block_tables, self.context_lens, self.w.scale,
+                                   p["shared_cols"], p["group_ptr"], p["group_members"],
+                                   p["group_col"], p["max_group_size"],
+                                   workspace=self.pfx_workspace,
+                                   partition_size=self.partition_size, stream=stream)
+        return self.out
+
     def step(self, stream=None):
         self.store(stream)
         self.attend(stream)

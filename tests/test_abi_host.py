@@ -188,6 +188,47 @@ def test_prefill_argument_validation(kw, status):
     assert _prefill_rc(**kw) == status
 
 
+def _prefix_rc(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=16, bt=FAKE, W=4, ctx=FAKE, B=2, Hq=16, Hkv=8,
+             D=128, bs=256, scale=0.1, dt=B.PKV_BF16, part=0, sc=FAKE, gp=FAKE, gm=FAKE, gc=FAKE,
+             G=1, mg=2, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return B.load_library().paged_attn_decode_prefix(
+        a["out"], a["q"], a["k"], a["v"], a["nb"], a["bt"], a["W"], a["ctx"], a["B"], a["Hq"],
+        a["Hkv"], a["D"], a["bs"], a["scale"], a["dt"], a["part"], a["sc"], a["gp"], a["gm"],
+        a["gc"], a["G"], a["mg"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=B.PKV_F32), -2),                  # the shared-block pass is bf16 MFMA
+    (dict(bs=32), -2), (dict(bs=16), -2),      # tiles of 64 keys
+    (dict(sc=None), -1), (dict(gp=None), -1), (dict(gm=None), -1), (dict(gc=None), -1),
+    (dict(G=-1), -1), (dict(mg=-3), -1), (dict(G=65536), -2), (dict(mg=64 * 65535 + 1), -2),
+    (dict(ws_bytes=1024), -3), (dict(ws=None), -3), (dict(D=96), -2), (dict(B=0), 0),
+    (dict(Hq=1 << 17, Hkv=1 << 17), -2),       # byte offsets of a tile must fit 31 bits
+])
+def test_decode_prefix_argument_validation(kw, status):
+    assert _prefix_rc(**kw) == status
+
+
+def test_decode_prefix_workspace_query():
+    # the decode call's bytes, rounded up to 256, plus (D + 2) floats per (sequence, head,
+    # table column) for the shared blocks' pieces
+    base = B.paged_attn_decode_workspace_bytes(512, 16, 128, 16, 256)
+    want = (base + 255) // 256 * 256 + 512 * 16 * 16 * 130 * 4
+    assert B.paged_attn_decode_prefix_workspace_bytes(512, 16, 128, 16, 256) == want
+    assert B.paged_attn_decode_prefix_workspace_bytes(0, 16, 128, 16, 256) == 0
+
+
+def test_prefix_groups_from_tables():
+    # one group per (column, block id) among each sequence's shared leading columns
+    bt = np.array([[7, 9, 3], [7, 9, 4], [7, 5, 6], [8, 1, 2]])
+    ptr, mem, col, largest = B.prefix_groups(bt, [2, 2, 1, 0])
+    groups = {(int(col[g]), tuple(mem[ptr[g]:ptr[g + 1]])) for g in range(len(col))}
+    assert groups == {(0, (0, 1, 2)), (1, (0, 1))}
+    assert largest == 3 and ptr[-1] == len(mem) == 5
+
+
 def test_store_argument_validation():
     lib = B.load_library()
     # stride below the row size, unsupported dtype, zero tokens (a no-op)

@@ -1,0 +1,104 @@
+"""GPU parity of paged_attn_decode_prefix (shared prefix blocks read once per group, bf16 MFMA)
+against the fp64 oracle, and against paged_attn_decode on the same step."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_225_amd import _binding as B
+from paged_kv_cache_225_amd.harness import DeviceStep
+from tests.oracle_pipeline import run_workload
+from tests.parity import assert_attention_close
+from workloads import make_config, make_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def prefix_run(w, shared_cols=None, split_groups=False, partition_size=0):
+    ds = DeviceStep(w, partition_size=partition_size)
+    ds.store()
+    p = ds.prefix_setup(shared_cols)
+    if split_groups:
+        # the same (column, block) members cut into two groups: a column with several groups
+        ptr = p["group_ptr"].cpu().numpy()
+        mem = p["group_members"].cpu().numpy()
+        col = p["group_col"].cpu().numpy()
+        nptr, ncol = [0], []
+        for g in range(len(col)):
+            lo, hi = int(ptr[g]), int(ptr[g + 1])
+            mid = (lo + hi) // 2
+            for a, b in ((lo, mid), (mid, hi)):
+                if b > a:
+                    nptr.append(b)
+                    ncol.append(col[g])
+        p["group_ptr"] = torch.tensor(nptr, dtype=torch.int32, device="cuda")
+        p["group_col"] = torch.tensor(ncol, dtype=torch.int32, device="cuda")
+    print(f"{w.name}: {len(p['group_col'])} groups, largest {p['max_group_size']}", flush=True)
+    ds.out.zero_()
+    ds.attend_prefix()
+    torch.cuda.synchronize()
+    return ds
+
+
+def test_decode_prefix_large_config_full():
+    """All 512 rows of the large decode workload (half the sequences sharing 2-8 leading
+    blocks of one resident prefix) through the shared-block pass, against the oracle."""
+    w = make_config(5)
+    ds = prefix_run(w)
+    ref, _, _, _ = run_workload(w)
+    st = assert_attention_close(ds.out_f64(), ref, rel_l2=1e-2, label="config5 prefix")
+    print(f"config 5 through the prefix call: {st}", flush=True)
+    sharers = np.nonzero(w.shared_blocks)[0]
+    assert_attention_close(ds.out_f64()[sharers], ref[sharers], label="config5 sharers")
+    # the plain call on the same step agrees within rounding (bf16 probabilities of the
+    # shared keys here, fp32 there)
+    plain = ds.out.float().clone()
+    ds.attend()
+    torch.cuda.synchronize()
+    d = (plain - ds.out.float()).abs().max().item()
+    assert d < 2e-2, d
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_decode_prefix_shapes(case):
+    # (D, Hq, Hkv, bs, seqs, shared blocks of a common prefix, peaked logits)
+    D, Hq, Hkv, bs, n, npb, qm = [
+        (128, 16, 8, 256, 70, 3, 1.0),   # more than 64 members per group (two chunks)
+        (64, 16, 2, 64, 40, 6, 1.0),     # GQA 8, blocks of 64 keys
+        (128, 8, 8, 128, 33, 4, 4.0),    # no head pairing (GQA 1), peaked logits
+        (128, 32, 8, 64, 20, 9, 1.0),    # GQA 4, several shared columns
+    ][case]
+    rng = np.random.default_rng(500 + case)
+    ctx = rng.integers(npb * bs + 1, npb * bs + 3 * bs, size=n)
+    shared = rng.integers(0, npb + 1, size=n)
+    shared = np.minimum(shared, (ctx - 1) // bs)
+    w = make_decode(600 + case, ctx, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16", bs=bs,
+                    shared_blocks=shared, n_prefix_blocks=npb, q_mult=qm, name=f"pfx{case}")
+    ds = prefix_run(w, split_groups=(case % 2 == 1))
+    ref, _, _, _ = run_workload(w)
+    assert_attention_close(ds.out_f64(), ref, rel_l2=1e-2, label=w.name)
+
+
+def test_decode_prefix_without_groups_matches_plain_call():
+    # no shared columns: no groups, the stream pass takes every key and every row merges
+    w = make_config(2)
+    ds = prefix_run(w, shared_cols=np.zeros(w.num_seqs, np.int32))
+    a = ds.out.clone()
+    ds.attend()
+    torch.cuda.synchronize()
+    assert (a.float() - ds.out.float()).abs().max().item() < 1e-2
+    ref, _, _, _ = run_workload(w)
+    assert_attention_close(ds.out_f64(), ref, rel_l2=1e-2, label="plain")
+
+
+def test_decode_prefix_partition_and_repeat():
+    # a forced partition size; two calls in a row give the same bits (stale slots unused)
+    w = make_config(5)
+    ds = prefix_run(w, partition_size=64)
+    a = ds.out.clone()
+    ds.attend_prefix()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), ds.out.view(torch.int16))
+    ref, _, _, _ = run_workload(w)
+    assert_attention_close(ds.out_f64(), ref, rel_l2=1e-2, label="partition 64")
