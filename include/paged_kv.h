@@ -236,10 +236,12 @@ int paged_attn_decode_noalloc(void* out, const void* q,
  *                group's member count (it sizes the launch).
  *   workspace    at least paged_attn_decode_prefix_workspace_bytes(...) bytes (the decode
  *                call's slots plus (D + 2) floats per (sequence, q head, table column)).
- * Preconditions: for every b and c < shared_cols[b], exactly one group with column c holds
- * b, and every member of a group holds the same block id in that column; shared_cols[b] *
- * bs <= context_lens[b] - 1 (the newest token's block is private). A column left without a
- * group is merged from whatever its slot holds.
+ * Preconditions: the (member, group column) pairs of the groups are exactly the pairs
+ * (b, c) with c < shared_cols[b], each once; every member of a group holds the same block
+ * id in that column; shared_cols[b] * bs <= context_lens[b] - 1 (the newest token's block
+ * is private). A column left without a group is merged from whatever its slot holds; a
+ * member, group column or shared_cols value out of range makes the kernels read and write
+ * outside their arrays. pkv_check_prefix (and PKV_DEBUG) names such mistakes.
  * Supported: bf16 only; block_size >= 64; Hkv * D < 2^24; num_groups <= 65535; the decode
  * call's other limits. Results equal paged_attn_decode's within rounding: the shared keys'
  * probabilities are rounded to bf16 for the MFMA, as in prefill. Errors as
@@ -472,9 +474,23 @@ int attn_prefill_varlen(void* out, const void* q,
  *                       block_tables (NULL for attn_prefill_varlen's packed keys) also
  *                       Lk <= max_blocks_per_seq * bs (CONTEXT_RANGE) and the first
  *                       ceil(Lk / bs) entries of each table in [0, num_blocks) (BLOCK_RANGE).
+ *   pkv_check_prefix    paged_attn_decode_prefix's groups, with the call's block_tables
+ *                       and context_lens: each shared_cols[b] in [0, max_blocks_per_seq] and,
+ *                       when above 0, shared_cols[b] * bs <= n_b - 1 (SHARED_COLS, index =
+ *                       b); group_ptr starts at 0, never decreases, no group holds more than
+ *                       max_group_size members and group_ptr[num_groups] is the number of
+ *                       shared pairs, the sum of shared_cols (GROUP_PTR, index = the entry);
+ *                       group_col[g] in [0, max_blocks_per_seq) (GROUP_COL, index = g); every
+ *                       member in [0, num_seqs) (GROUP_MEMBER, index = its entry in
+ *                       group_members); the (member, group_col[g]) pairs are exactly the
+ *                       pairs (b, c) with c < shared_cols[b], each once (PREFIX_COVER, index
+ *                       = b, value = c, at the entry that repeats a pair or names a column
+ *                       outside b's shared ones); the members of a group hold one block id
+ *                       in its column (GROUP_BLOCK, index = the entry, value = its id).
  * PKV_DEBUG: when this environment variable is set to a non-empty value other than "0" at
  * the library's first device call, store_kvcache, paged_attn_decode,
- * paged_attn_decode_store, paged_attn_prefill_varlen and attn_prefill_varlen run the
+ * paged_attn_decode_store, paged_attn_decode_prefix (the decode check, then the prefix
+ * check), paged_attn_prefill_varlen and attn_prefill_varlen run the
  * matching check on their device arrays (on_device 1) after their argument checks and
  * return its status without enqueuing anything when it fails. Such calls synchronise their
  * stream; while the stream records a graph the check is skipped. paged_attn_decode_noalloc
@@ -488,7 +504,13 @@ enum {
   PKV_CHECK_NEW_TOKEN_SLOT = 5,
   PKV_CHECK_CU_SEQLENS = 6,
   PKV_CHECK_LK_LT_LQ = 7,
-  PKV_CHECK_MAX_SEQLEN = 8
+  PKV_CHECK_MAX_SEQLEN = 8,
+  PKV_CHECK_SHARED_COLS = 9,
+  PKV_CHECK_GROUP_PTR = 10,
+  PKV_CHECK_GROUP_COL = 11,
+  PKV_CHECK_GROUP_MEMBER = 12,
+  PKV_CHECK_PREFIX_COVER = 13,
+  PKV_CHECK_GROUP_BLOCK = 14
 };
 
 typedef struct pkv_violation {
@@ -509,6 +531,12 @@ int pkv_check_prefill(const int32_t* block_tables, int32_t max_blocks_per_seq,
                       int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
                       int32_t max_seqlen_k, int32_t num_blocks, int32_t block_size,
                       int32_t on_device, hipStream_t stream, pkv_violation* first);
+int pkv_check_prefix(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                     const int32_t* shared_cols, const int32_t* group_ptr,
+                     const int32_t* group_members, const int32_t* group_col, int32_t num_groups,
+                     int32_t max_group_size, int32_t on_device, hipStream_t stream,
+                     pkv_violation* first);
 
 /* ------------------------------------------------------------------------------------
  * Temperature sampling - [P3] section 4.3 采样器 (Sampler.forward); [P1] SamplingParams

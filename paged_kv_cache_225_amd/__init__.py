@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     paged_attn_prefill_varlen,
     pkv_block_hash,
     pkv_check_decode,
+    pkv_check_prefix,
     pkv_check_prefill,
     pkv_check_store,
     pkv_decode_metadata,
@@ -40,5 +41,5 @@ __all__ = [
     "paged_attn_decode_workspace_bytes", "paged_attn_prefill_varlen", "pkv_decode_metadata",
     "pkv_block_hash", "pkv_prefill_metadata", "pkv_sample", "pkv_sample_workspace_bytes",
     "pkv_status_string", "pkv_xxh64", "store_kvcache", "PreconditionError", "pkv_check_decode",
-    "pkv_check_prefill", "pkv_check_store",
+    "pkv_check_prefill", "pkv_check_prefix", "pkv_check_store",
 ]

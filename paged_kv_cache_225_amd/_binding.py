@@ -82,6 +82,8 @@ SIGNATURES = {
     "pkv_bm_remove_sequence": (_c_int, [_p, _i32]),
     "pkv_check_store": (_c_int, [_p, _i32, _i64, _i32, _p, _p]),
     "pkv_check_decode": (_c_int, [_p, _i32, _p, _p, _i32, _i32, _i32, _i32, _p, _p]),
+    "pkv_check_prefix": (_c_int, [_p, _i32, _p, _i32, _i32, _p, _p, _p, _p, _i32, _i32, _i32,
+                                  _p, _p]),
     "pkv_check_prefill": (_c_int, [_p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _p, _p]),
     "attn_prefill_varlen": (_c_int, [_p, _p, _p, _i64, _p, _i64, _p, _p, _i32, _i32, _i32, _i32,
@@ -100,7 +102,9 @@ class PagedKVError(RuntimeError):
 
 PKV_ERR_PRECONDITION = -5
 CHECK_NAMES = {1: "SLOT_RANGE", 2: "SLOT_DUPLICATE", 3: "CONTEXT_RANGE", 4: "BLOCK_RANGE",
-               5: "NEW_TOKEN_SLOT", 6: "CU_SEQLENS", 7: "LK_LT_LQ", 8: "MAX_SEQLEN"}
+               5: "NEW_TOKEN_SLOT", 6: "CU_SEQLENS", 7: "LK_LT_LQ", 8: "MAX_SEQLEN",
+               9: "SHARED_COLS", 10: "GROUP_PTR", 11: "GROUP_COL", 12: "GROUP_MEMBER",
+               13: "PREFIX_COVER", 14: "GROUP_BLOCK"}
 
 
 class pkv_violation(ctypes.Structure):
@@ -455,6 +459,25 @@ def pkv_check_prefill(cu_seqlens_q, cu_seqlens_k, total_q, max_seqlen_q, max_seq
                                           int(block_size), on_dev,
                                           _stream(stream) if on_dev else None, ctypes.byref(v))
     _run_check("pkv_check_prefill", rc, v)
+
+
+
+def pkv_check_prefix(block_tables, context_lens, block_size, shared_cols, group_ptr,
+                     group_members, group_col, max_group_size, stream=None):
+    """paged_attn_decode_prefix's groups against the call's tables and lengths (the groups
+    count is len(group_col))."""
+    arrs = [_arr_ptr(a) for a in (block_tables, context_lens, shared_cols, group_ptr,
+                                  group_members, group_col)]
+    t, c, sc, gp, gm, gc = arrs
+    on_dev = _on_device(*arrs)
+    n = len(context_lens)
+    width = block_tables.shape[1] if n else 1
+    v = pkv_violation()
+    rc = load_library().pkv_check_prefix(t[0], width, c[0], n, int(block_size), sc[0], gp[0],
+                                         gm[0], gc[0], len(group_col), int(max_group_size),
+                                         on_dev, _stream(stream) if on_dev else None,
+                                         ctypes.byref(v))
+    _run_check("pkv_check_prefix", rc, v)
 
 
 class DecodeGraphs:

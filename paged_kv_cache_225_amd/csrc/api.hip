@@ -345,6 +345,13 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
                                      fused ? slot_mapping : nullptr, num_seqs, num_blocks,
                                      block_size, 1, stream, nullptr);
     if (chk != PKV_OK) return chk;
+    if (sp) {
+      const int pchk = pkv_check_prefix(block_tables, max_blocks_per_seq, context_lens,
+                                        num_seqs, block_size, sp->cols, sp->group_ptr,
+                                        sp->group_members, sp->group_col, sp->num_groups,
+                                        sp->max_group_size, 1, stream, nullptr);
+      if (pchk != PKV_OK) return pchk;
+    }
   }
   pkv::DecodeArgs a;
   a.out = out;

@@ -225,4 +225,83 @@ int pkv_check_prefill(const int32_t* block_tables, int32_t max_blocks_per_seq,
   return PKV_OK;
 }
 
+
+// The groups of a shared-prefix decode call. Every entry of group_members is a pair
+// (sequence, column group_col[g]); these pairs must be exactly the pairs (b, c) with
+// c < shared_cols[b], each once, and the members of a group must hold one block id in
+// their column (a prefix cache reuses a block only in the column its tokens occupy).
+int pkv_check_prefix(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                     const int32_t* shared_cols, const int32_t* group_ptr,
+                     const int32_t* group_members, const int32_t* group_col, int32_t num_groups,
+                     int32_t max_group_size, int32_t on_device, hipStream_t stream,
+                     pkv_violation* first) {
+  clear(first);
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_groups < 0 || max_group_size < 0)
+    return PKV_ERR_INVALID;
+  if (!pow2_at_least_16(block_size)) return PKV_ERR_INVALID;
+  if (num_seqs > 0 && (!block_tables || !context_lens || !shared_cols)) return PKV_ERR_INVALID;
+  if (num_groups > 0 && (!group_ptr || !group_col)) return PKV_ERR_INVALID;
+  const int32_t W = max_blocks_per_seq;
+  std::vector<int32_t> tb, cb, sb, pb, mb, gb;
+  const int32_t *t = nullptr, *c = nullptr, *sc = nullptr, *ptr = nullptr, *mem = nullptr,
+                *col = nullptr;
+  int rc = host_view(context_lens, num_seqs, on_device, stream, cb, &c);
+  if (rc == PKV_OK) rc = host_view(shared_cols, num_seqs, on_device, stream, sb, &sc);
+  if (rc == PKV_OK) rc = host_view(block_tables, (int64_t)num_seqs * W, on_device, stream, tb, &t);
+  if (rc == PKV_OK && num_groups > 0)
+    rc = host_view(group_ptr, (int64_t)num_groups + 1, on_device, stream, pb, &ptr);
+  if (rc == PKV_OK && num_groups > 0) rc = host_view(group_col, num_groups, on_device, stream, gb, &col);
+  if (rc != PKV_OK) return rc;
+  // shared columns: whole blocks before the newest token's, inside the table
+  int64_t pairs = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t s = sc[b];
+    if (s < 0 || s > W || (s > 0 && s * block_size > (int64_t)c[b] - 1))
+      return fail(first, PKV_CHECK_SHARED_COLS, b, s);
+    pairs += s;
+  }
+  int64_t total = 0;
+  if (num_groups > 0) {
+    if (ptr[0] != 0) return fail(first, PKV_CHECK_GROUP_PTR, 0, ptr[0]);
+    for (int32_t g = 0; g < num_groups; ++g) {
+      const int64_t size = (int64_t)ptr[g + 1] - ptr[g];
+      if (size < 0 || size > max_group_size || ptr[g + 1] > pairs)
+        return fail(first, PKV_CHECK_GROUP_PTR, (int64_t)g + 1, ptr[g + 1]);
+      if (col[g] < 0 || col[g] >= W) return fail(first, PKV_CHECK_GROUP_COL, g, col[g]);
+    }
+    total = ptr[num_groups];
+  }
+  if (total != pairs) return fail(first, PKV_CHECK_GROUP_PTR, num_groups, total);
+  if (total == 0) return PKV_OK;
+  if (!group_members) return PKV_ERR_INVALID;
+  rc = host_view(group_members, total, on_device, stream, mb, &mem);
+  if (rc != PKV_OK) return rc;
+  // pair (b, c) -> seen; as many pairs as entries, so a repeat or a pair outside the
+  // shared columns is found at the entry that makes it
+  std::vector<int64_t> base;
+  std::vector<uint8_t> seen;
+  try {
+    base.resize((size_t)num_seqs + 1);
+    seen.assign((size_t)pairs, 0);
+  } catch (const std::bad_alloc&) {
+    return PKV_ERR_INVALID;
+  }
+  base[0] = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) base[b + 1] = base[b] + sc[b];
+  for (int32_t g = 0; g < num_groups; ++g) {
+    int32_t block = 0;
+    for (int64_t e = ptr[g]; e < ptr[g + 1]; ++e) {
+      const int32_t b = mem[e];
+      if (b < 0 || b >= num_seqs) return fail(first, PKV_CHECK_GROUP_MEMBER, e, b);
+      if (col[g] >= sc[b] || seen[base[b] + col[g]]) return fail(first, PKV_CHECK_PREFIX_COVER, b, col[g]);
+      seen[base[b] + col[g]] = 1;
+      const int32_t id = t[(int64_t)b * W + col[g]];
+      if (e == ptr[g]) block = id;
+      else if (id != block) return fail(first, PKV_CHECK_GROUP_BLOCK, e, id);
+    }
+  }
+  return PKV_OK;  // pairs entries, none repeated: every shared pair is covered
+}
+
 }  // extern "C"

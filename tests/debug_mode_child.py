@@ -23,7 +23,7 @@ from paged_kv_cache_225_amd import _binding as B  # noqa: E402
 from paged_kv_cache_225_amd.harness import DeviceStep, GraphDecodeStep  # noqa: E402
 from tests.oracle_pipeline import run_workload  # noqa: E402
 from tests.parity import assert_attention_close  # noqa: E402
-from workloads import make_config, make_prefill  # noqa: E402
+from workloads import make_config, make_decode, make_prefill  # noqa: E402
 
 
 def expect_precondition(label, fn, *tensors):
@@ -104,6 +104,43 @@ def main():
         lambda: B.paged_attn_prefill_varlen(dp.out, dp.q, dp.k_cache, dp.v_cache,
                                             dp.block_tables, dp.cu_seqlens_q, cu_k,
                                             dp.max_seqlen_q, dp.max_seqlen_k, wp.scale), dp.out)
+
+    # shared-prefix decode: valid groups compute; a member outside the batch and a member
+    # holding another block in the group's column are rejected before any launch
+    rng = np.random.default_rng(41)
+    ctx = rng.integers(3 * 64 + 1, 6 * 64, size=24)
+    shared = np.minimum(rng.integers(0, 4, size=24), (ctx - 1) // 64)
+    wx = make_decode(42, ctx, Hq=16, Hkv=8, D=128, dtype="bf16", bs=64, shared_blocks=shared,
+                     n_prefix_blocks=3, name="debug prefix")
+    refx, _, _, _ = run_workload(wx)
+    dx = DeviceStep(wx)
+    dx.store()
+    pf = dx.prefix_setup()
+    dx.attend_prefix()
+    torch.cuda.synchronize()
+    assert_attention_close(dx.out_f64(), refx, rel_l2=1e-2, label="prefix decode")
+    print("debug mode: valid shared-prefix decode computed", flush=True)
+    mem = pf["group_members"].clone()
+    mem[0] = wx.num_seqs
+    dx.out.fill_(5.0)
+    expect_precondition(
+        "decode_prefix, member outside the batch",
+        lambda: B.paged_attn_decode_prefix(dx.out, dx.q, dx.k_cache, dx.v_cache, dx.block_tables,
+                                           dx.context_lens, wx.scale, pf["shared_cols"],
+                                           pf["group_ptr"], mem, pf["group_col"],
+                                           pf["max_group_size"], workspace=dx.pfx_workspace),
+        dx.out)
+    g = int(np.argmax(np.diff(pf["group_ptr"].cpu().numpy())))
+    e = int(pf["group_ptr"][g]) + 1
+    bt = dx.block_tables.clone()
+    bt[int(pf["group_members"][e]), int(pf["group_col"][g])] += 1
+    expect_precondition(
+        "decode_prefix, member holding another block",
+        lambda: B.paged_attn_decode_prefix(dx.out, dx.q, dx.k_cache, dx.v_cache, bt,
+                                           dx.context_lens, wx.scale, pf["shared_cols"],
+                                           pf["group_ptr"], pf["group_members"], pf["group_col"],
+                                           pf["max_group_size"], workspace=dx.pfx_workspace),
+        dx.out)
 
     # graphs record with the checks skipped and replay correctly
     ds = DeviceStep(w, table_width=4)

@@ -161,6 +161,67 @@ void metadata(Rng& rng) {
 }
 
 // ------------------------------------------------------------------ precondition checks
+// Shared-prefix groups: a valid set built from random tables (one group per (column, block)
+// among the shared columns), then at most one mutation; every array has its exact size. A
+// passing verdict is confirmed by counting each (sequence, column) pair's cover directly.
+void prefix_groups(Rng& rng) {
+  pkv_violation v;
+  for (int trial = 0; trial < 3000; ++trial) {
+    const int32_t B = (int32_t)rng.range(1, 7), W = (int32_t)rng.range(1, 5), bs = 16;
+    std::vector<int32_t> bt((size_t)B * W), ctx(B), sc(B);
+    for (auto& x : bt) x = (int32_t)rng.range(0, 3);
+    for (int b = 0; b < B; ++b) {
+      ctx[b] = (int32_t)rng.range(0, W * bs);
+      sc[b] = ctx[b] > 0 ? (int32_t)rng.range(0, (ctx[b] - 1) / bs) : 0;
+    }
+    std::vector<int32_t> ptr{0}, mem, col;
+    for (int32_t c = 0; c < W; ++c)
+      for (int32_t id = 0; id <= 3; ++id) {
+        const size_t start = mem.size();
+        for (int32_t b = 0; b < B; ++b)
+          if (c < sc[b] && bt[(size_t)b * W + c] == id) mem.push_back(b);
+        if (mem.size() > start) {
+          ptr.push_back((int32_t)mem.size());
+          col.push_back(c);
+        }
+      }
+    const int32_t G = (int32_t)col.size();
+    int32_t largest = 0;
+    for (int32_t g = 0; g < G; ++g) largest = std::max(largest, ptr[g + 1] - ptr[g]);
+    const int kind = (int)rng.range(0, 7);
+    if (kind == 1) sc[rng.range(0, B - 1)] = (int32_t)rng.range(-1, W + 1);
+    if (kind == 2 && G > 0) ptr[rng.range(0, G)] += (int32_t)rng.range(-2, 2);
+    if (kind == 3 && G > 0) col[rng.range(0, G - 1)] = (int32_t)rng.range(-1, W);
+    if (kind == 4 && !mem.empty()) mem[rng.range(0, mem.size() - 1)] = (int32_t)rng.range(-1, B);
+    if (kind == 5) bt[rng.range(0, bt.size() - 1)] = (int32_t)rng.range(0, 3);
+    if (kind == 6) largest = std::max(0, largest - 1);
+    if (mem.empty()) mem.push_back(0);  // a valid address; no entry is read then
+    const int r = pkv_check_prefix(bt.data(), W, ctx.data(), B, bs, sc.data(), ptr.data(),
+                                   mem.data(), G ? col.data() : nullptr, G, largest, 0, nullptr,
+                                   &v);
+    CHECK(r == PKV_OK || r == PKV_ERR_PRECONDITION);
+    if (r == PKV_ERR_PRECONDITION) {
+      CHECK(v.check >= PKV_CHECK_SHARED_COLS && v.check <= PKV_CHECK_GROUP_BLOCK);
+      continue;
+    }
+    std::vector<int> cover((size_t)B * W, 0);
+    for (int32_t g = 0; g < G; ++g) {
+      CHECK(ptr[g + 1] - ptr[g] <= largest && col[g] >= 0 && col[g] < W);
+      for (int32_t e = ptr[g]; e < ptr[g + 1]; ++e) {
+        CHECK(mem[e] >= 0 && mem[e] < B);
+        CHECK(bt[(size_t)mem[e] * W + col[g]] == bt[(size_t)mem[ptr[g]] * W + col[g]]);
+        ++cover[(size_t)mem[e] * W + col[g]];
+      }
+    }
+    for (int32_t b = 0; b < B; ++b) {
+      CHECK(sc[b] >= 0 && sc[b] <= W && (sc[b] == 0 || sc[b] * bs <= ctx[b] - 1));
+      for (int32_t c = 0; c < W; ++c) CHECK(cover[(size_t)b * W + c] == (c < sc[b] ? 1 : 0));
+    }
+  }
+  CHECK(pkv_check_prefix(nullptr, 1, nullptr, 2, 16, nullptr, nullptr, nullptr, nullptr, 0, 0,
+                         0, nullptr, &v) == PKV_ERR_INVALID);
+}
+
 void checks(Rng& rng) {
   pkv_violation v;
   for (int trial = 0; trial < 3000; ++trial) {
@@ -207,6 +268,7 @@ void checks(Rng& rng) {
   CHECK(pkv_check_store(nullptr, 3, 10, 0, nullptr, &v) == PKV_ERR_INVALID);
   CHECK(pkv_check_decode(nullptr, 1, nullptr, nullptr, 2, 1, 16, 0, nullptr, &v) ==
         PKV_ERR_INVALID);
+  prefix_groups(rng);
 }
 
 // ------------------------------------------------------------------ hashing
@@ -371,6 +433,17 @@ void device_argument_errors() {
                                   0.1f, 0, PKV_BF16, nullptr) == PKV_ERR_UNSUPPORTED);
   CHECK(attn_prefill_varlen(F, F, F, 100, F, 1024, I, I, 4, 100, 64, 64, 16, 8, 128, 0.1f, 1,
                             PKV_BF16, nullptr) == PKV_ERR_INVALID);
+  // the prefix call: bf16 and blocks of 64 keys or more; its slots widen the workspace
+  const size_t pneed = paged_attn_decode_prefix_workspace_bytes(4, 16, 128, 16, 256, 0);
+  CHECK(pneed > paged_attn_decode_workspace_bytes(4, 16, 128, 16, 256, 0));
+  CHECK(paged_attn_decode_prefix(F, F, F, F, 16, I, 16, I, 4, 16, 8, 128, 256, 0.1f, PKV_F32, 0,
+                                 I, I, I, I, 1, 1, F, pneed, nullptr) == PKV_ERR_UNSUPPORTED);
+  CHECK(paged_attn_decode_prefix(F, F, F, F, 16, I, 16, I, 4, 16, 8, 128, 32, 0.1f, PKV_BF16, 0,
+                                 I, I, I, I, 1, 1, F, pneed, nullptr) == PKV_ERR_UNSUPPORTED);
+  CHECK(paged_attn_decode_prefix(F, F, F, F, 16, I, 16, I, 4, 16, 8, 128, 256, 0.1f, PKV_BF16, 0,
+                                 I, I, I, I, 1, 1, F, pneed - 1, nullptr) == PKV_ERR_WORKSPACE);
+  CHECK(paged_attn_decode_prefix(F, F, F, F, 16, I, 16, I, 4, 16, 8, 128, 256, 0.1f, PKV_BF16, 0,
+                                 I, nullptr, I, I, 1, 1, F, pneed, nullptr) == PKV_ERR_INVALID);
   pkv_decode_graphs* g = nullptr;
   void* arr[3] = {F, F, F};
   CHECK(pkv_decode_graphs_create_layers(&g, 4, 0, arr, (const void* const*)arr,

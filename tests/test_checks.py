@@ -210,3 +210,99 @@ def test_check_argument_errors():
     assert lib.pkv_check_prefill(None, 0, None, None, 0, 0, 0, 0, 0, 0, 0, None,
                                  B.ctypes.byref(v)) == 0
     assert v.check == 0
+
+
+def _prefix_case():
+    """The large decode workload's metadata (half the sequences sharing 2-8 leading blocks of
+    one resident prefix) and its groups as paged_attn_decode_prefix takes them."""
+    w = _decode_like(5)
+    md = _decode_md(w)
+    sc = np.asarray(w.shared_blocks, np.int32)
+    ptr, mem, col, largest = B.prefix_groups(md["block_tables"], sc)
+    return w, md, dict(block_tables=md["block_tables"], context_lens=md["context_lens"],
+                       block_size=w.block_size, shared_cols=sc, group_ptr=ptr,
+                       group_members=mem, group_col=col, max_group_size=largest)
+
+
+def _prefix_check(args, **kw):
+    a = dict(args)
+    a.update(kw)
+    B.pkv_check_prefix(**a)
+
+
+def test_prefix_groups_of_the_workload_pass():
+    w, md, args = _prefix_case()
+    assert len(args["group_col"]) > 0 and args["max_group_size"] > 1
+    _prefix_check(args)
+    # no shared columns, no groups
+    z = np.zeros(0, np.int32)
+    _prefix_check(args, shared_cols=np.zeros(w.num_seqs, np.int32), group_ptr=np.zeros(1, np.int32),
+                  group_members=z, group_col=z, max_group_size=0)
+    # a group cut in two (one column with two groups of one block) is still a valid cover
+    ptr, col = args["group_ptr"], args["group_col"]
+    g = int(np.argmax(np.diff(ptr)))
+    mid = (int(ptr[g]) + int(ptr[g + 1])) // 2
+    ptr2 = np.insert(ptr, g + 1, mid).astype(np.int32)
+    col2 = np.insert(col, g, col[g]).astype(np.int32)
+    _prefix_check(args, group_ptr=ptr2, group_col=col2)
+
+
+def test_prefix_violations():
+    w, md, args = _prefix_case()
+    sc, ptr, mem, col = (args[k] for k in ("shared_cols", "group_ptr", "group_members",
+                                           "group_col"))
+    bs, W, ctx = w.block_size, md["block_tables"].shape[1], md["context_lens"]
+    # shared columns: inside the table and before the newest token's block
+    s2 = sc.copy(); s2[11] = W + 1
+    assert _violation(_prefix_check, args, shared_cols=s2) == ("SHARED_COLS", 11, W + 1)
+    s2 = sc.copy(); s2[12] = -1
+    assert _violation(_prefix_check, args, shared_cols=s2) == ("SHARED_COLS", 12, -1)
+    b = int(np.nonzero(sc)[0][0])
+    s2 = sc.copy(); s2[b] = (int(ctx[b]) - 1) // bs + 1  # would take the newest token's block
+    assert _violation(_prefix_check, args, shared_cols=s2) == ("SHARED_COLS", b, int(s2[b]))
+    # group_ptr: starts at 0, never decreases, groups within max_group_size, ends at the
+    # number of shared pairs
+    p2 = ptr.copy(); p2[0] = 1
+    assert _violation(_prefix_check, args, group_ptr=p2) == ("GROUP_PTR", 0, 1)
+    p2 = ptr.copy(); p2[3] = p2[2] - 1
+    assert _violation(_prefix_check, args, group_ptr=p2) == ("GROUP_PTR", 3, int(p2[3]))
+    big = int(np.argmax(np.diff(ptr)))
+    assert _violation(_prefix_check, args, max_group_size=args["max_group_size"] - 1) == \
+        ("GROUP_PTR", big + 1, int(ptr[big + 1]))
+    p2 = ptr.copy(); p2[-1] -= 1
+    assert _violation(_prefix_check, args, group_ptr=p2, group_members=mem[:-1].copy()) == \
+        ("GROUP_PTR", len(col), int(p2[-1]))
+    # a group column outside the table, a member outside the batch
+    c2 = col.copy(); c2[4] = W
+    assert _violation(_prefix_check, args, group_col=c2) == ("GROUP_COL", 4, W)
+    m2 = mem.copy(); m2[7] = w.num_seqs
+    assert _violation(_prefix_check, args, group_members=m2) == ("GROUP_MEMBER", 7, w.num_seqs)
+    # a pair named twice: the second entry of a group repeats its first member
+    g = big
+    e = int(ptr[g]) + 1
+    m2 = mem.copy(); m2[e] = m2[e - 1]
+    assert _violation(_prefix_check, args, group_members=m2) == \
+        ("PREFIX_COVER", int(mem[e - 1]), int(col[g]))
+    # a member that does not share that column (its own block there), in place of one that does
+    private = int(np.nonzero(sc == 0)[0][0])
+    m2 = mem.copy(); m2[e] = private
+    assert _violation(_prefix_check, args, group_members=m2) == \
+        ("PREFIX_COVER", private, int(col[g]))
+    # a member holding another block in the group's column
+    t2 = md["block_tables"].copy()
+    t2[int(mem[e]), int(col[g])] += 1
+    assert _violation(_prefix_check, args, block_tables=t2) == \
+        ("GROUP_BLOCK", e, int(t2[int(mem[e]), int(col[g])]))
+
+
+def test_prefix_check_argument_errors():
+    lib = B.load_library()
+    assert lib.pkv_check_prefix(None, 4, None, 2, 256, None, None, None, None, 0, 0, 0, None,
+                                None) == -1
+    p = np.zeros(8, np.int32).ctypes.data
+    assert lib.pkv_check_prefix(p, 4, p, 2, 100, p, p, p, p, 1, 1, 0, None, None) == -1
+    assert lib.pkv_check_prefix(p, 4, p, 2, 256, p, None, p, p, 1, 1, 0, None, None) == -1
+    assert lib.pkv_check_prefix(p, 4, p, 2, 256, p, p, p, p, -1, 1, 0, None, None) == -1
+    # an empty batch with no groups passes
+    assert lib.pkv_check_prefix(None, 4, None, 0, 256, None, None, None, None, 0, 0, 0, None,
+                                None) == 0
