@@ -544,7 +544,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b64_hbm_traffic.json")
 def decode_sources_sha256():
     import hashlib
     h = hashlib.sha256()
-    for f in ("common.hpp", "launch.hpp", "decode.hip"):
+    for f in ("common.hpp", "launch.hpp", "prefix_unit.hpp", "decode.hip"):
         with open(os.path.join(ROOT, "paged_kv_cache_225_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

@@ -45,6 +45,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "prefix_unit.hpp"
 
 namespace pkv {
 
@@ -56,6 +57,19 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ int clamp_ctx(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
 
+// The shared blocks' work units as extra workgroups behind the stream shares (UNITS).
+struct PrefixUnits {
+  const int32_t* g_ptr;
+  const int32_t* g_members;
+  const int32_t* g_col;
+  float* pfx_o;
+  float* pfx_ml;
+  int32_t num_heads;
+  int32_t n_hg;        // head groups per kv row (q heads / the unit's heads)
+  int32_t num_groups;
+  int32_t n_stream;    // workgroups 0 .. n_stream - 1 own the stream shares
+};
+
 // One chunk of a wavefront's share: keys [k, k + cnt) of segment (b, g).
 struct Chunk {
   int x;          // position of the chunk's first key on the line
@@ -66,18 +80,44 @@ struct Chunk {
 };
 
 // PFX: kv_stream_from[b] is the count of sequence b's leading table columns shared with
-// other sequences of the call, whose keys another kernel takes (decode_prefix_kernel): the
-// line holds only the keys past them, all read non-temporally, and every segment leaves
-// partials for the combine.
-template <typename T, int D, int G, int NI, int HPW, bool NT, bool PFX = false>
-__global__ __launch_bounds__(256) void decode_stream_kernel(
+// other sequences of the call, whose keys decode_prefix_unit takes: the line holds only the
+// keys past them, all read non-temporally, and every segment leaves partials for the
+// combine.
+// UNITS (with PFX): one grid for the whole prefix-mode pass. Workgroups below pu.n_stream
+// are the stream shares; the rest are decode_prefix_unit work units, head group fastest.
+// The dispatcher starts workgroups in index order, so the units take the slots that the
+// first shares to finish leave free while the last shares still stream. Batches of 512
+// sequences, half sharing 2-8 leading blocks of 256 keys, went from 281-287 us per call
+// with the units as a second kernel after this one to 271.5-276.3 us (flushed cache, same
+// process, two parts), bitwise the same output; the second kernel on a forked stream,
+// joined by events, took 287-291 us. The units need the two-wavefronts-per-SIMD register
+// bound (256 VGPRs), which spills the stream shares of 8 q heads per kv head, and their
+// 64 KB of LDS tiles (D = 128) next to the stream shares' per-sequence table must leave
+// room for two workgroups per CU; calls outside either limit launch the units as their own
+// kernel.
+template <typename T, int D, int G, int NI, int HPW, bool NT, bool PFX = false,
+          bool UNITS = false>
+__global__ __launch_bounds__(256, UNITS ? 2 : 1) void decode_stream_kernel(
     T* __restrict__ out, const T* __restrict__ q, const T* __restrict__ k_cache,
     const T* __restrict__ v_cache, int32_t num_blocks, const int32_t* __restrict__ block_tables,
     int32_t bt_stride, const int32_t* __restrict__ context_lens, int32_t num_seqs,
     int32_t num_kv_heads, int32_t bs_log2, float scale_log2e, int32_t min_keys,
     int32_t max_pieces, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     int32_t* __restrict__ ws_meta, int32_t skip_last,
-    const int32_t* __restrict__ kv_stream_from) {
+    const int32_t* __restrict__ kv_stream_from, PrefixUnits pu) {
+  if constexpr (UNITS) {
+    static_assert(PFX && Elem<T>::kBytes == 2, "the shared-block units are bf16 MFMA");
+    if ((int)blockIdx.x >= pu.n_stream) {
+      const int u = (int)blockIdx.x - pu.n_stream;
+      const int hg = u % pu.n_hg, rest = u / pu.n_hg;
+      decode_prefix_unit<D, (G % 2 == 0 ? 2 : 1)>(
+          hg, rest % pu.num_groups, rest / pu.num_groups, (const __bf16*)q,
+          (const __bf16*)k_cache, (const __bf16*)v_cache, num_blocks, block_tables, bt_stride,
+          pu.g_ptr, pu.g_members, pu.g_col, pu.num_heads, num_kv_heads, bs_log2, scale_log2e,
+          pu.pfx_o, pu.pfx_ml);
+      return;
+    }
+  }
   using E = Elem<T>;
   constexpr bool kBF16 = E::kBytes == 2;
   constexpr int EPL = E::kPerChunk;  // elements per 16-byte lane chunk
@@ -118,7 +158,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   const int Hq = Hkv * G;
   const int mult = HPW > 0 ? 1 : Hkv;  // line positions per key of a sequence
   const int total = mult * s_cum[num_seqs];
-  const int n_waves = HPW > 0 ? gridDim.x : gridDim.x * 4;  // share owners
+  const int n_owner_blocks = UNITS ? pu.n_stream : (int)gridDim.x;
+  const int n_waves = HPW > 0 ? n_owner_blocks : n_owner_blocks * 4;  // share owners
   int S = (total + n_waves - 1) / n_waves;
   S = S < min_keys ? min_keys : S;
   if (blockIdx.x == 0) {  // publish the split for the combine kernel
@@ -801,21 +842,60 @@ static int run_decode(const DecodeArgs& a, hipStream_t stream) {
   auto* stream_kernel = a.kv_stream_from ? decode_stream_kernel<T, D, G, NI, HPW, true>
                                          : decode_stream_kernel<T, D, G, NI, HPW, false>;
   constexpr bool kPrefixMode = Elem<T>::kBytes == 2;  // the shared-block pass is bf16 MFMA
-  if constexpr (kPrefixMode) {
-    if (a.prefix) stream_kernel = decode_stream_kernel<T, D, G, NI, HPW, true, true>;
+  // the shared-block units ride in the stream grid when its register bound fits the stream
+  // shares (not with 8 q heads per kv head) and two workgroups per CU still fit in LDS with
+  // the units' tiles (D = 128: up to 4095 sequences)
+  bool units_in_grid = false;
+  if constexpr (kPrefixMode && G <= 4) {
+    units_in_grid = a.prefix != 0 &&
+                    2 * (kPrefixUnitLds<D> + lds) <= (size_t)kLdsPerCu;
   }
-  hipLaunchKernelGGL(stream_kernel, dim3((unsigned)blocks), dim3(256),
-                     lds, stream, (T*)a.out, (const T*)a.q, (const T*)a.k_cache,
-                     (const T*)a.v_cache, a.num_blocks, a.block_tables, a.max_blocks_per_seq,
-                     a.context_lens, a.num_seqs, a.num_kv_heads, bs_log2, c, a.partition,
-                     a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, a.new_k != nullptr ? 1 : 0,
-                     a.kv_stream_from);
+  if constexpr (kPrefixMode) {
+    if (a.prefix && !units_in_grid) stream_kernel = decode_stream_kernel<T, D, G, NI, HPW, true, true>;
+  }
+  if (!units_in_grid) {
+    hipLaunchKernelGGL(stream_kernel, dim3((unsigned)blocks), dim3(256),
+                       lds, stream, (T*)a.out, (const T*)a.q, (const T*)a.k_cache,
+                       (const T*)a.v_cache, a.num_blocks, a.block_tables, a.max_blocks_per_seq,
+                       a.context_lens, a.num_seqs, a.num_kv_heads, bs_log2, c, a.partition,
+                       a.max_parts, a.ws_o, a.ws_ml, a.ws_meta, a.new_k != nullptr ? 1 : 0,
+                       a.kv_stream_from, PrefixUnits{});
+  }
   PrefixParts pp{};
   if constexpr (kPrefixMode) {
     if (a.prefix) {
-      if (hipGetLastError() != hipSuccess) return -4;
-      const int rc = launch_decode_prefix(a.pfx, stream);
-      if (rc != 0) return rc;
+      if (units_in_grid) {
+        if constexpr (G <= 4) {
+          constexpr int GH = G % 2 == 0 ? 2 : 1;
+          PrefixUnits pu;
+          pu.g_ptr = a.pfx.group_ptr;
+          pu.g_members = a.pfx.group_members;
+          pu.g_col = a.pfx.group_col;
+          pu.pfx_o = a.pfx.pfx_o;
+          pu.pfx_ml = a.pfx.pfx_ml;
+          pu.num_heads = a.num_heads;
+          pu.n_hg = a.num_heads / GH;
+          pu.num_groups = a.pfx.num_groups;
+          pu.n_stream = (int32_t)blocks;
+          const int64_t units = a.pfx.num_groups > 0 && a.pfx.max_group_size > 0
+                                    ? (int64_t)pu.n_hg * a.pfx.num_groups *
+                                          ((a.pfx.max_group_size + 63) / 64)
+                                    : 0;
+          if (blocks + units > 0x7FFFFFFF) return -2;
+          hipLaunchKernelGGL((decode_stream_kernel<T, D, G, NI, HPW, true, true, true>),
+                             dim3((unsigned)(blocks + units)), dim3(256), lds, stream,
+                             (T*)a.out, (const T*)a.q, (const T*)a.k_cache,
+                             (const T*)a.v_cache, a.num_blocks, a.block_tables,
+                             a.max_blocks_per_seq, a.context_lens, a.num_seqs, a.num_kv_heads,
+                             bs_log2, c, a.partition, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta,
+                             a.new_k != nullptr ? 1 : 0, a.kv_stream_from, pu);
+        }
+        if (hipGetLastError() != hipSuccess) return -4;
+      } else {
+        if (hipGetLastError() != hipSuccess) return -4;
+        const int rc = launch_decode_prefix(a.pfx, stream);
+        if (rc != 0) return rc;
+      }
       pp = PrefixParts{a.kv_stream_from, a.pfx.pfx_o, a.pfx.pfx_ml, a.max_blocks_per_seq, bs_log2};
     }
   }

@@ -62,7 +62,9 @@ def test_decode_prefix_large_config_full():
 
 @pytest.mark.parametrize("case", range(4))
 def test_decode_prefix_shapes(case):
-    # (D, Hq, Hkv, bs, seqs, shared blocks of a common prefix, peaked logits)
+    # (D, Hq, Hkv, bs, seqs, shared blocks of a common prefix, peaked logits); the units ride
+    # in the stream kernel's grid except with 8 q heads per kv head (case 1), where they run
+    # as their own kernel
     D, Hq, Hkv, bs, n, npb, qm = [
         (128, 16, 8, 256, 70, 3, 1.0),   # more than 64 members per group (two chunks)
         (64, 16, 2, 64, 40, 6, 1.0),     # GQA 8, blocks of 64 keys
@@ -102,3 +104,24 @@ def test_decode_prefix_partition_and_repeat():
     assert torch.equal(a.view(torch.int16), ds.out.view(torch.int16))
     ref, _, _, _ = run_workload(w)
     assert_attention_close(ds.out_f64(), ref, rel_l2=1e-2, label="partition 64")
+
+
+@pytest.mark.parametrize("n", [4095, 4096])
+def test_decode_prefix_either_side_of_the_grid_lds_limit(n):
+    """D = 128: up to 4095 sequences the shared-block units ride in the stream kernel's grid
+    (their 64 KB of LDS tiles and the shares' 4-byte-per-sequence table leave room for two
+    workgroups per CU); from 4096 on they run as their own kernel. Both against the oracle
+    and against the plain call on the same step."""
+    rng = np.random.default_rng(808)
+    ctx = rng.integers(3 * 64 + 1, 6 * 64, size=n)
+    shared = np.minimum(rng.integers(0, 4, size=n), (ctx - 1) // 64)
+    w = make_decode(809, ctx, Hq=2, Hkv=1, D=128, dtype="bf16", bs=64, shared_blocks=shared,
+                    n_prefix_blocks=3, name=f"pfx_many{n}")
+    ds = prefix_run(w)
+    ref, _, _, _ = run_workload(w)
+    assert_attention_close(ds.out_f64(), ref, rel_l2=1e-2, label=w.name)
+    a = ds.out.float().clone()
+    ds.attend()
+    torch.cuda.synchronize()
+    assert (a - ds.out.float()).abs().max().item() < 2e-2
+
