@@ -125,3 +125,41 @@ def test_decode_prefix_either_side_of_the_grid_lds_limit(n):
     torch.cuda.synchronize()
     assert (a - ds.out.float()).abs().max().item() < 2e-2
 
+
+
+@pytest.mark.parametrize("cfg", ["units_in_grid", "units_kernel"])
+def test_decode_prefix_recorded_in_a_graph(cfg):
+    """The prefix call recorded into a HIP graph (through torch's capture) and replayed
+    three times, with eager calls of the library between the replays: every replay gives
+    the eager call's bits. Both launch forms: the units in the stream grid (2 q heads per kv
+    head) and the units as their own kernel (8 q heads per kv head)."""
+    Hq, Hkv = (16, 8) if cfg == "units_in_grid" else (16, 2)
+    rng = np.random.default_rng(901)
+    ctx = rng.integers(4 * 64 + 1, 10 * 64, size=48)
+    shared = np.minimum(rng.integers(0, 5, size=48), (ctx - 1) // 64)
+    w = make_decode(902, ctx, Hq=Hq, Hkv=Hkv, D=128, dtype="bf16", bs=64, shared_blocks=shared,
+                    n_prefix_blocks=4, name=f"pfx_graph_{cfg}")
+    ds = prefix_run(w)
+    eager = ds.out.clone()
+    ref, _, _, _ = run_workload(w)
+    assert_attention_close(ds.out_f64(), ref, rel_l2=1e-2, label=w.name)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ds.attend_prefix(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ds.attend_prefix(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ds.out.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ds.out.view(torch.int16), eager.view(torch.int16)), rep
+        ds.attend()  # eager library work between replays (plain call, same workspace region)
+        torch.cuda.synchronize()
+        print(f"{w.name}: replay {rep} equal to the eager call", flush=True)
+    del g
