@@ -67,15 +67,29 @@ def prefill_flops(w):
 # ---------------------------------------------------------------- GPU legs
 class CacheFlush:
     """A 1 GiB device buffer rewritten between timed runs (outside the timed region), so that
-    every run starts with the 256 MB last-level cache and the L2s holding none of its inputs."""
+    every run starts with the 256 MB last-level cache and the L2s holding none of its inputs.
 
-    def __init__(self, torch, nbytes=1 << 30):
+    read_back: also read the buffer back, so that no dirty line is left either. After the
+    write alone the caches hold up to ~290 MB of the buffer's dirty lines, whose write-back
+    lands inside the timed call; for an HBM-bound call that is time the call's own traffic
+    does not account for (batch-512 shared-prefix decode, one process: 275.8-277.6 us after
+    the write alone, 265.5-268.0 after write and read-back, 259 us with no flush). The
+    compute-bound prefill calls gain nothing from it (varlen 74.0-74.6 us after the write,
+    74.8-75.5 after a read alone) and lose 2-5% after the longer write-and-read flush, so the
+    prefill legs keep the write alone."""
+
+    def __init__(self, torch, nbytes=1 << 30, read_back=False):
+        self.torch = torch
+        self.read_back = read_back
         self.buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+        self.sink = torch.empty((), dtype=torch.int64, device="cuda")
         self.val = 0
 
     def __call__(self):
         self.val += 1
         self.buf.fill_(self.val)
+        if self.read_back:
+            self.torch.sum(self.buf, dim=0, dtype=self.torch.int64, out=self.sink)
 
 
 class HipTimer:
@@ -368,6 +382,10 @@ def bench_large_decode(torch, iters, warmup, flush=None):
             "frac_hbm_unique": uniq / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "tokens_per_s": w.num_seqs / (med * 1e-3), "shared_hist": w.meta.get("shared_hist"),
             "kv_stream_from": "per sequence: its count of shared leading blocks",
+            "cold_cache": None if flush is None else
+            ("each timed call after a 1 GiB write and read-back (no input and no dirty line "
+             "left in the caches)" if flush.read_back else
+             "each timed call after a 1 GiB write (no input left in the caches)"),
             "split": split, "prefix_call": prefix}
 
 
@@ -655,10 +673,11 @@ def main():
         return
     if args.only is not None:
         flush = None if args.no_flush else CacheFlush(torch)
+        dflush = None if args.no_flush else CacheFlush(torch, read_back=True)
         if args.only == "large":
-            res = bench_large_decode(torch, args.iters, 5, flush)
+            res = bench_large_decode(torch, args.iters, 5, dflush)
         elif args.only == "tiny":
-            res = bench_tiny_decode(torch, args.iters, 5, flush)
+            res = bench_tiny_decode(torch, args.iters, 5, dflush)
         elif args.only == "prefill3packed":
             res = bench_prefill_packed(torch, args.iters, 5, flush)
         elif args.only == "chunked":
@@ -706,21 +725,23 @@ def main():
     }
     if not args.no_secondary:
         flush = None if args.no_flush else CacheFlush(torch)
+        dflush = None if args.no_flush else CacheFlush(torch, read_back=True)
         line["secondary_timing"] = ("HIP events around each call on its stream; median of "
                                     f"{args.iters} runs after 5 warm-up calls and "
                                     f"{SECONDARY_WARMUP_S} s more of the workload's own calls "
                                     "(steady-state clocks); "
                                     + ("no flush" if flush is None else
-                                       "a 1 GiB buffer rewritten before each timed run"))
+                                       "a 1 GiB buffer rewritten before each timed run (the "
+                                       "decode legs also read it back, leaving no dirty line)"))
         print("bench: prefill workloads", file=sys.stderr, flush=True)
         line["prefill"] = [bench_prefill(torch, 3, args.iters, 5, flush),
                            bench_prefill(torch, 4, args.iters, 5, flush),
                            bench_prefill_packed(torch, args.iters, 5, flush),
                            bench_prefill(torch, "chunked", args.iters, 5, flush)]
         print("bench: large decode workload", file=sys.stderr, flush=True)
-        line["large_decode"] = bench_large_decode(torch, args.iters, 5, flush)
+        line["large_decode"] = bench_large_decode(torch, args.iters, 5, dflush)
         print("bench: tiny decode workload", file=sys.stderr, flush=True)
-        line["tiny_decode"] = bench_tiny_decode(torch, args.iters, 5, flush)
+        line["tiny_decode"] = bench_tiny_decode(torch, args.iters, 5, dflush)
         print("bench: graph-replayed small-batch decode", file=sys.stderr, flush=True)
         line["graph_decode"] = bench_graph_decode(torch, 200)
         print("bench: graph-replayed 28-layer decode steps", file=sys.stderr, flush=True)

@@ -473,7 +473,7 @@ __device__ __forceinline__ void bits_to_float(const typename LaneBits<T, DPL>::t
 // into more pieces (a share then covers a few hundred keys), and 4 for larger ones, where
 // most rows have one or two pieces and 16 speculative rows per row would be mostly wasted.
 // PFX: besides the stream kernel's pieces, row (b, h) merges one piece per shared leading
-// table column of sequence b (pp.cols[b] of them), left by decode_prefix_kernel.
+// table column of sequence b (pp.cols[b] of them), left by the decode_prefix_unit work units.
 template <typename T, int D, int kSpec, bool PFX = false>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     T* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t cap,

@@ -72,7 +72,7 @@ struct DecodeArgs {
   const int32_t* slot_mapping;
   int64_t num_slots;
   // prefix mode: kv_stream_from[b] is sequence b's count of shared leading table columns,
-  // whose keys decode_prefix_kernel takes (pfx); the stream kernel takes the rest
+  // whose keys the decode_prefix_unit work units take (pfx); the stream kernel takes the rest
   int32_t prefix;
   PrefixArgs pfx;
 };
