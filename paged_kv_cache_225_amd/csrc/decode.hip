@@ -471,7 +471,8 @@ __device__ __forceinline__ void bits_to_float(const typename LaneBits<T, DPL>::t
 // per lane (one coalesced row per load instruction). A row cut into at most kSpec pieces
 // needs no second round. kSpec is 16 for calls of at most 128 sequences, whose rows are cut
 // into more pieces (a share then covers a few hundred keys), and 4 for larger ones, where
-// most rows have one or two pieces and 16 speculative rows per row would be mostly wasted.
+// most rows have one or two pieces and 16 speculative rows per row would be mostly wasted
+// (1 for larger ones in prefix mode, whose rows merge their shared pieces later anyway).
 // PFX: besides the stream kernel's pieces, row (b, h) merges one piece per shared leading
 // table column of sequence b (pp.cols[b] of them), left by the decode_prefix_unit work units.
 template <typename T, int D, int kSpec, bool PFX = false>
@@ -913,14 +914,19 @@ static int run_decode(const DecodeArgs& a, hipStream_t stream) {
   nt.scale_log2e = c;
   const dim3 cgrid((unsigned)((rows + 3) / 4));
   if constexpr (kPrefixMode) {
-    if (a.prefix) {  // the shared blocks' pieces merge in the one-wavefront-per-row form
+    // the shared blocks' pieces merge in the one-wavefront-per-row form. Larger calls load
+    // one o row in the first round, not four: every row then merges its shared pieces in
+    // later rounds anyway, and the 3 extra rows per row were mostly unused reads (batch 512,
+    // half the sequences sharing 2-8 blocks: 266.3-267.0 -> 265.0-266.9 us per call, four
+    // alternating reps, bitwise the same output)
+    if (a.prefix) {
       if (a.num_seqs <= kCombineSpec16Seqs)
         hipLaunchKernelGGL((decode_combine_kernel<T, D, 16, true>), cgrid, dim3(256), 0, stream,
                            (T*)a.out, a.context_lens, (int32_t)cap, rows, a.num_heads,
                            a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta,
                            HPW > 0 ? 1 : 0, nt, pp);
       else
-        hipLaunchKernelGGL((decode_combine_kernel<T, D, 4, true>), cgrid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((decode_combine_kernel<T, D, 1, true>), cgrid, dim3(256), 0, stream,
                            (T*)a.out, a.context_lens, (int32_t)cap, rows, a.num_heads,
                            a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.ws_meta,
                            HPW > 0 ? 1 : 0, nt, pp);
