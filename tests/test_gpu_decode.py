@@ -251,3 +251,29 @@ def test_decode_split_report_reads_the_calls_layout():
     cum = np.concatenate([[0], np.cumsum(np.asarray(w.seq_lens, dtype=np.int64))])
     inner = sum(1 for k in range(1, shares) if k * S not in set(cum.tolist()))
     assert sum(p * n for p, n in hist.items()) == w.num_seqs + inner
+
+
+@pytest.mark.parametrize("n,dtype,fused", [(64, "bf16", False), (65, "bf16", False),
+                                           (1100, "bf16", False), (1100, "f32", True),
+                                           (2049, "bf16", True)])
+def test_decode_length_scan_either_side_of_the_staged_prologue(n, dtype, fused):
+    """Up to 64 sequences every workgroup loads the context lengths directly; above that all
+    its threads first stage them in LDS in batches of 1024 sequences (1100: two batches,
+    the second with 76 lengths; 2049: three, the last with one). Both forms against the
+    oracle, plain and fused-store calls."""
+    rng = np.random.default_rng(1300 + n)
+    ctx = rng.integers(1, 700, size=n)
+    if dtype == "bf16":
+        w = make_decode(1400 + n, ctx, Hq=4, Hkv=2, D=128, dtype="bf16", bs=64, name=f"scan{n}")
+    else:
+        w = make_decode(1400 + n, ctx, Hq=4, Hkv=2, D=64, dtype="f32", bs=64, name=f"scan{n}")
+    ds = DeviceStep(w)
+    if fused:
+        ds.step_fused()
+    else:
+        ds.step()
+    torch.cuda.synchronize()
+    ref, _, _, _ = run_workload(w)
+    atol, l2 = (1e-4, 1e-5) if dtype == "f32" else (2e-2, 1e-2)
+    st = assert_attention_close(ds.out_f64(), ref, atol=atol, rel_l2=l2, label=w.name)
+    print(f"{w.name} ({'fused' if fused else 'plain'}): {st}", flush=True)
