@@ -872,12 +872,17 @@ static int run_decode(const DecodeArgs& a, hipStream_t stream) {
                                          : decode_stream_kernel<T, D, G, NI, HPW, false>;
   constexpr bool kPrefixMode = Elem<T>::kBytes == 2;  // the shared-block pass is bf16 MFMA
   // the shared-block units ride in the stream grid when its register bound fits the stream
-  // shares (not with 8 q heads per kv head) and two workgroups per CU still fit in LDS with
-  // the units' tiles (D = 128: up to 4095 sequences)
+  // shares (not with 8 q heads per kv head), two workgroups per CU still fit in LDS with the
+  // units' tiles (D = 128: up to 4095 sequences) and the 1-D grid holds them all
   bool units_in_grid = false;
+  int64_t units = 0;  // the units' workgroups (some exit at once: groups below the largest)
   if constexpr (kPrefixMode && G <= 4) {
+    if (a.prefix && a.pfx.num_groups > 0 && a.pfx.max_group_size > 0)
+      units = (int64_t)(a.num_heads / (G % 2 == 0 ? 2 : 1)) * a.pfx.num_groups *
+              ((a.pfx.max_group_size + 63) / 64);
     units_in_grid = a.prefix != 0 &&
-                    2 * (kPrefixUnitLds<D> + lds) <= (size_t)kLdsPerCu;
+                    2 * (kPrefixUnitLds<D> + lds) <= (size_t)kLdsPerCu &&
+                    blocks + units <= 0x7FFFFFFF;
   }
   if constexpr (kPrefixMode) {
     if (a.prefix && !units_in_grid) stream_kernel = decode_stream_kernel<T, D, G, NI, HPW, true, true>;
@@ -906,11 +911,6 @@ static int run_decode(const DecodeArgs& a, hipStream_t stream) {
           pu.n_hg = a.num_heads / GH;
           pu.num_groups = a.pfx.num_groups;
           pu.n_stream = (int32_t)blocks;
-          const int64_t units = a.pfx.num_groups > 0 && a.pfx.max_group_size > 0
-                                    ? (int64_t)pu.n_hg * a.pfx.num_groups *
-                                          ((a.pfx.max_group_size + 63) / 64)
-                                    : 0;
-          if (blocks + units > 0x7FFFFFFF) return -2;
           hipLaunchKernelGGL((decode_stream_kernel<T, D, G, NI, HPW, true, true, true>),
                              dim3((unsigned)(blocks + units)), dim3(256), lds, stream,
                              (T*)a.out, (const T*)a.q, (const T*)a.k_cache,
