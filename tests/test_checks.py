@@ -306,3 +306,44 @@ def test_prefix_check_argument_errors():
     # an empty batch with no groups passes
     assert lib.pkv_check_prefix(None, 4, None, 0, 256, None, None, None, None, 0, 0, 0, None,
                                 None) == 0
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_prefix_groups_builder_satisfies_the_check(seed):
+    """prefix_groups' output for random tables with shared leading blocks passes
+    pkv_check_prefix, and so do the same groups with their members and the groups
+    themselves reordered (a cover does not depend on order)."""
+    rng = np.random.Generator(np.random.PCG64(900 + seed))
+    n = int(rng.integers(1, 40))
+    bs = int(rng.choice([64, 128, 256]))
+    W = int(rng.integers(2, 9))
+    ctx = rng.integers(1, W * bs + 1, size=n).astype(np.int32)
+    npfx = int(rng.integers(1, W))
+    prefix_ids = rng.permutation(10_000)[:npfx].astype(np.int32)
+    sc = np.minimum(rng.integers(0, npfx + 1, size=n), (ctx - 1) // bs).astype(np.int32)
+    sc[ctx == 0] = 0
+    bt = np.full((n, W), -1, np.int32)
+    nxt = 10_000
+    for b in range(n):
+        used = -(-int(ctx[b]) // bs)
+        for c in range(used):
+            if c < sc[b]:
+                bt[b, c] = prefix_ids[c]
+            else:
+                bt[b, c] = nxt
+                nxt += 1
+    ptr, mem, col, largest = B.prefix_groups(bt, sc)
+    args = dict(block_tables=bt, context_lens=ctx, block_size=bs, shared_cols=sc,
+                group_ptr=ptr, group_members=mem, group_col=col, max_group_size=largest)
+    _prefix_check(args)
+    assert len(mem) == int(sc.sum())
+    # reorder members inside each group, then the groups themselves
+    mem2 = mem.copy()
+    for g in range(len(col)):
+        lo, hi = int(ptr[g]), int(ptr[g + 1])
+        mem2[lo:hi] = rng.permutation(mem2[lo:hi])
+    order = rng.permutation(len(col))
+    sizes = np.diff(ptr)[order]
+    ptr3 = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    mem3 = np.concatenate([mem2[ptr[g]:ptr[g + 1]] for g in order] or [np.zeros(0, np.int32)]).astype(np.int32)
+    _prefix_check(args, group_ptr=ptr3, group_members=mem3, group_col=col[order].astype(np.int32))
